@@ -1,0 +1,273 @@
+"""fp64 CPU oracle of the WISE working-set attention path.
+
+TEST INFRASTRUCTURE ONLY.  This package is imported by ``tests/``, by
+``__graft_entry__.smoke()`` and by the ``cpu_baseline`` leg of ``bench.py``,
+and by nothing else.  It shares no code with the HIP library: it neither
+imports it nor is imported by it.  The GPU path must never fall back to it.
+
+What it computes is the plain definition from "Attention Routing Stabilizes
+Early: Working-Set Inference for Recurrent Language Models" (WISE), written
+out in float64 with numpy, in the order the paper states it:
+
+* Section 3, Eq. (2): masked softmax attention A = softmax(Q K^T / sqrt(d_h) + M),
+  O = A V, with M the causal mask (key j admissible for query i iff j <= i).
+* Section 5.1, Eq. (5): block mass r_qb = (1/|I_q|) sum_{i in I_q} sum_{j in I_b} A_ij.
+* Section 5.1, Eq. (6) (right-hand part) and Appendix A.1, Eq. (12): the
+  cumulative-eta block support, the smallest set of admissible key blocks
+  whose mass reaches eta.  Here it is applied once to the mean of the block
+  masses over the discovery steps, then the sink block 0 and the diagonal
+  block q are added (readings listed below).
+* Section 5.2, Eq. (7)-(8): working-set mask R and late-step attention
+  softmax(Q K^T / sqrt(d_h) + M + R) V.
+* Appendix A.1, Eq. (13): identification margins delta_rank, delta_minus,
+  delta_plus and Delta_q, used to tell near-tie rows from decided ones.
+
+Readings where the paper leaves a step open (all of them also written out
+with their reasons in the design notes):
+
+1. Discovery steps are combined by averaging r over the td dense steps, then
+   one selection runs on the mean (the temporal union of per-step supports is
+   a separate variant).
+2. Ties in the ranking are broken by the lower key-block index.
+3. The threshold test is inclusive (mass >= eta), in float64.
+4. Sink (block 0) and diagonal (block q) are added after the eta selection and
+   do not count toward eta; the cap, if any, limits only the eta-ranked part.
+5. |I_q| = B for every block (sequence lengths are multiples of B); the
+   diagonal block's mass counts only admissible keys j <= i.
+6. If rounding leaves the total admissible mass below eta, every admissible
+   block is kept.
+
+Inputs are float64 arrays (``bf16_to_f64`` widens bf16 bits exactly).
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "bf16_to_f64", "default_scale", "attention_weights", "attention_output",
+    "dense_attention", "block_mass", "block_mass_rows", "mean_block_mass",
+    "select_support", "support_margins", "working_set_mask",
+    "masked_attention_weights", "masked_attention", "trajectory_head",
+]
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Widen raw bf16 bits (uint16) exactly to float64."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def default_scale(head_dim: int) -> float:
+    """1/sqrt(d_h), the softmax temperature of Eq. (2)."""
+    return 1.0 / math.sqrt(head_dim)
+
+
+def _rows(S: int, rows) -> np.ndarray:
+    return np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+
+
+def _softmax_rows(s: np.ndarray) -> np.ndarray:
+    """Row softmax of a logit matrix whose inadmissible entries are -inf."""
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def attention_weights(q, k, scale: float, rows=None) -> np.ndarray:
+    """Rows ``rows`` of A = softmax(q k^T * scale + M), Eq. (2), causal M.
+
+    q, k: float64 [S, D] of one (batch, head).  Returns [len(rows), S];
+    entry (i, j) is zero for j > i.
+    """
+    S = k.shape[0]
+    r = _rows(S, rows)
+    s = (q[r] @ k.T) * scale
+    causal = np.arange(S)[None, :] > r[:, None]          # M_ij = -inf for j > i
+    s[causal] = -np.inf
+    return _softmax_rows(s)
+
+
+def attention_output(a, v) -> np.ndarray:
+    """O = A V, Eq. (2)."""
+    return a @ v
+
+
+def dense_attention(q, k, v, scale: Optional[float] = None, rows=None) -> np.ndarray:
+    """Dense causal attention output rows, Eq. (2)."""
+    if scale is None:
+        scale = default_scale(q.shape[1])
+    return attention_output(attention_weights(q, k, scale, rows), v)
+
+
+def block_mass_rows(a_q, block: int) -> np.ndarray:
+    """Eq. (5) for one query block: r_qb for every key block b.
+
+    ``a_q`` holds the B rows of A belonging to query block q ([B, S]); the
+    result has S/B entries, r_qb = (1/B) sum_{i in I_q} sum_{j in I_b} A_ij.
+    """
+    B = block
+    nb = a_q.shape[1] // B
+    per_row_block = a_q.reshape(a_q.shape[0], nb, B).sum(axis=2)   # sum over j in I_b
+    return per_row_block.sum(axis=0) / a_q.shape[0]                 # (1/|I_q|) sum over i in I_q
+
+
+def block_mass(q, k, scale: float, block: int, qblocks=None) -> np.ndarray:
+    """Block-mass matrix r[q, b] of one (batch, head) at one step, Eq. (5).
+
+    Returns [len(qblocks), S/B] (all query blocks by default).
+    """
+    S = k.shape[0]
+    nb = S // block
+    qbs = range(nb) if qblocks is None else qblocks
+    out = []
+    for qb in qbs:
+        rows = np.arange(qb * block, (qb + 1) * block)
+        out.append(block_mass_rows(attention_weights(q, k, scale, rows), block))
+    return np.array(out)
+
+
+def mean_block_mass(step_masses: Sequence[np.ndarray]) -> np.ndarray:
+    """Equal-weight mean of r over the discovery steps (reading 1)."""
+    acc = np.zeros_like(np.asarray(step_masses[0], dtype=np.float64))
+    for r in step_masses:
+        acc = acc + r
+    return acc / len(step_masses)
+
+
+def _ranked(mbar_row, q: int) -> List[int]:
+    """Admissible blocks 0..q ordered by mass descending, index ascending (reading 2)."""
+    return sorted(range(q + 1), key=lambda b: (-float(mbar_row[b]), b))
+
+
+def select_support(mbar_row, q: int, eta: float, cap: int = 0) -> List[int]:
+    """Working set of query block q, ascending block ids.
+
+    Eq. (6) / Eq. (12): k* is the smallest k whose k largest masses sum to at
+    least eta; the top-k* blocks (capped at ``cap`` when cap > 0) are taken,
+    then the sink block 0 and the diagonal block q are added (reading 4).
+    """
+    order = _ranked(mbar_row, q)
+    prefix = 0.0
+    k_star = len(order)                  # reading 6: keep all if eta is never reached
+    for k, b in enumerate(order, start=1):
+        prefix += float(mbar_row[b])
+        if prefix >= eta:                # reading 3: inclusive
+            k_star = k
+            break
+    k = min(k_star, cap) if cap > 0 else k_star
+    chosen = set(order[:k]) | {0, q}
+    return sorted(chosen)
+
+
+def support_margins(mbar_row, q: int, eta: float) -> Dict[str, float]:
+    """Identification margins of Appendix A.1, Eq. (13), for one row.
+
+    delta_rank = (m_(k*) - m_(k*+1)) / 2 (inf when k* is the last block),
+    delta_minus = eta - sum_{s<k*} m_(s), delta_plus = sum_{s<=k*} m_(s) - eta,
+    Delta = min(delta_rank, delta_minus/(k*-1), delta_plus/k*).
+    """
+    order = _ranked(mbar_row, q)
+    vals = [float(mbar_row[b]) for b in order]
+    prefix = 0.0
+    k_star = len(vals)
+    for k, v in enumerate(vals, start=1):
+        prefix += v
+        if prefix >= eta:
+            k_star = k
+            break
+    before = sum(vals[: k_star - 1])
+    through = before + vals[k_star - 1]
+    d_rank = (vals[k_star - 1] - vals[k_star]) / 2 if k_star < len(vals) else math.inf
+    d_minus = eta - before
+    d_plus = through - eta
+    delta = min(d_rank, d_minus / (k_star - 1) if k_star > 1 else math.inf,
+                d_plus / k_star)
+    return {"k_star": k_star, "delta_rank": d_rank, "delta_minus": d_minus,
+            "delta_plus": d_plus, "Delta": delta}
+
+
+def working_set_mask(support_row: Sequence[int], S: int, block: int, rows) -> np.ndarray:
+    """Eq. (7) restricted to query rows in one query block: 0 if b(j) in W, else -inf."""
+    keep = np.zeros(S // block, dtype=bool)
+    keep[list(support_row)] = True
+    allowed = np.repeat(keep, block)                  # b(j) in W_{q(i)}
+    R = np.where(allowed, 0.0, -np.inf)
+    return np.broadcast_to(R, (len(rows), S))
+
+
+def masked_attention_weights(q, k, scale: float, block: int, supports: Dict[int, Sequence[int]],
+                             rows) -> np.ndarray:
+    """Rows of softmax(q k^T * scale + M + R), Eq. (8).
+
+    ``supports`` maps query block -> key blocks kept for it.  A row whose
+    support holds no admissible key returns zeros (no such row arises from
+    ``select_support``, which always keeps the diagonal block).
+    """
+    S = k.shape[0]
+    r = _rows(S, rows)
+    s = (q[r] @ k.T) * scale
+    s[np.arange(S)[None, :] > r[:, None]] = -np.inf                 # M
+    for i, row in enumerate(r):
+        s[i] += working_set_mask(supports[int(row) // block], S, block, [row])[0]   # R
+    out = np.zeros_like(s)
+    live = np.isfinite(s).any(axis=1)
+    if live.any():
+        out[live] = _softmax_rows(s[live])
+    return out
+
+
+def masked_attention(q, k, v, supports, block: int, scale: Optional[float] = None,
+                     rows=None) -> np.ndarray:
+    """Late-step output O~ = A~ V, Eq. (8)."""
+    if scale is None:
+        scale = default_scale(q.shape[1])
+    return attention_output(masked_attention_weights(q, k, scale, block, supports, rows), v)
+
+
+def trajectory_head(steps_qkv, td: int, block: int, eta: float, cap: int = 0,
+                    qblocks=None, scale: Optional[float] = None, out_rows: bool = True):
+    """Whole discover-early / reuse-late trajectory of one (batch, head).
+
+    ``steps_qkv`` yields float64 (q, k, v) per recurrent step t = 0..T-1.
+    Steps t < td are dense (Eq. 2) and contribute r^(t) (Eq. 5); the supports
+    are chosen once from the mean mass (Eq. 6 + readings); steps t >= td
+    recompute attention inside the frozen support (Eq. 7-8).  Only query
+    blocks ``qblocks`` are evaluated (all by default).
+
+    Returns dict with per-step outputs for the evaluated rows, the summed
+    mass (the same quantity a caller accumulates over the td steps), the
+    mean mass, the supports and their margins.
+    """
+    outputs, masses, supports, margins = [], [], {}, {}
+    qbs = None
+    for t, (q, k, v) in enumerate(steps_qkv):
+        S, D = q.shape
+        sc = default_scale(D) if scale is None else scale
+        nb = S // block
+        if qbs is None:
+            qbs = list(range(nb)) if qblocks is None else [int(x) for x in qblocks]
+        rows = np.concatenate([np.arange(qb * block, (qb + 1) * block) for qb in qbs])
+        if t < td:
+            a = attention_weights(q, k, sc, rows)
+            masses.append(np.array([block_mass_rows(a[i * block:(i + 1) * block], block)
+                                    for i in range(len(qbs))]))
+            outputs.append(attention_output(a, v) if out_rows else None)
+        else:
+            if not supports:
+                mbar = mean_block_mass(masses)
+                for i, qb in enumerate(qbs):
+                    supports[qb] = select_support(mbar[i], qb, eta, cap)
+                    margins[qb] = support_margins(mbar[i], qb, eta)
+            outputs.append(masked_attention(q, k, v, supports, block, sc, rows)
+                           if out_rows else None)
+    mass_sum = None
+    if masses:
+        mass_sum = np.zeros_like(masses[0])
+        for r in masses:
+            mass_sum = mass_sum + r
+    return {"qblocks": qbs, "outputs": outputs, "mass_sum": mass_sum,
+            "mass_mean": mean_block_mass(masses) if masses else None,
+            "supports": supports, "margins": margins}

@@ -1,0 +1,486 @@
+"""Pins of the fp64 oracle against what the WISE paper and mathematics fix.
+
+Every check here is independent of the oracle's own code path: closed forms
+(uniform attention, constant values, the logistic two-key case), invariants
+(rows sum to one, logit shift invariance, full support reproduces dense
+attention), brute-force subset enumeration for the selection rule, the
+perturbation property of Appendix A.1, and hand-derived golden fixtures.
+The mutation tests at the end plant typical mistakes into copies of the
+oracle's functions and require at least one pin to fail for each.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+from types import SimpleNamespace
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _impl(**over):
+    ns = SimpleNamespace(attention_weights=oracle.attention_weights,
+                         block_mass_rows=oracle.block_mass_rows,
+                         select_support=oracle.select_support,
+                         masked_attention_weights=oracle.masked_attention_weights)
+    for k, v in over.items():
+        setattr(ns, k, v)
+    return ns
+
+
+def _rand(seed, S, D):
+    g = np.random.default_rng(seed)
+    return (g.standard_normal((S, D)), g.standard_normal((S, D)), g.standard_normal((S, D)))
+
+
+# --------------------------------------------------------------------------
+# Pin functions (take an implementation namespace so mutants can be checked)
+# --------------------------------------------------------------------------
+
+def pin_uniform_when_q_zero(impl):
+    """Eq. (2) with Q = 0: every admissible key gets weight 1/(i+1)."""
+    S, D = 37, 8
+    _, k, v = _rand(1, S, D)
+    q = np.zeros((S, D))
+    a = impl.attention_weights(q, k, 0.3)
+    o = a @ v
+    expect = np.cumsum(v, axis=0) / np.arange(1, S + 1)[:, None]
+    np.testing.assert_allclose(o, expect, rtol=0, atol=1e-13)
+
+
+def pin_constant_values(impl):
+    S, D = 23, 5
+    q, k, _ = _rand(2, S, D)
+    v = np.full((S, D), 2.75)
+    o = impl.attention_weights(q, k, 0.7) @ v
+    np.testing.assert_allclose(o, 2.75, rtol=0, atol=1e-13)
+
+
+def pin_single_position(impl):
+    q, k, v = _rand(3, 1, 4)
+    o = impl.attention_weights(q, k, 0.5) @ v
+    np.testing.assert_allclose(o, v, rtol=0, atol=0)
+
+
+def pin_logistic_two_keys(impl):
+    """Row 1 over keys {0, 1}: A_11 = logistic((s_11 - s_10) * scale)."""
+    q = np.array([[0.4], [1.3]])
+    k = np.array([[-0.8], [0.6]])
+    scale = 0.9
+    a = impl.attention_weights(q, k, scale)
+    expect = expit((q[1, 0] * k[1, 0] - q[1, 0] * k[0, 0]) * scale)
+    assert abs(a[1, 1] - expect) < 1e-15
+    assert abs(a[1, 0] - (1 - expect)) < 1e-15
+
+
+def pin_causal_rows_sum_to_one(impl):
+    S, D = 40, 6
+    q, k, _ = _rand(4, S, D)
+    a = impl.attention_weights(q, k, 0.4)
+    np.testing.assert_allclose(a.sum(axis=1), 1.0, rtol=0, atol=1e-13)
+    assert np.all(a[np.triu_indices(S, 1)] == 0.0)
+    assert np.all(a[np.tril_indices(S)] > 0.0)
+
+
+def pin_key_shift_invariance(impl):
+    """Adding one vector c to every key shifts row i's logits by q_i.c: A unchanged."""
+    S, D = 29, 7
+    q, k, _ = _rand(5, S, D)
+    c = np.random.default_rng(6).standard_normal(D)
+    a0 = impl.attention_weights(q, k, 0.35)
+    a1 = impl.attention_weights(q, k + c, 0.35)
+    np.testing.assert_allclose(a0, a1, rtol=0, atol=1e-12)
+
+
+def pin_scale_is_a_temperature(impl):
+    S, D = 19, 4
+    q, k, _ = _rand(7, S, D)
+    a0 = impl.attention_weights(q, k, 0.5)
+    a1 = impl.attention_weights(2.0 * q, k, 0.25)
+    np.testing.assert_allclose(a0, a1, rtol=0, atol=1e-13)
+    a2 = impl.attention_weights(q, k, 1.0)
+    assert np.max(np.abs(a2 - a0)) > 1e-3
+
+
+def _frac(s):
+    return float(Fraction(s))
+
+
+def _golden_dense():
+    with open(os.path.join(GOLDEN, "dense_closed_form.json")) as f:
+        g = json.load(f)
+    qmap = {"0": 0.0, "ln2": math.log(2.0), "ln3": math.log(3.0)}
+    q = np.array([[qmap[x]] for x in g["q"]])
+    k = np.array(g["k"])[:, None]
+    v = np.array(g["v"])[:, None]
+    A = np.array([[_frac(x) for x in row] for row in g["A"]])
+    O = np.array([_frac(x) for x in g["O"]])
+    r = np.array([[_frac(x) for x in row] for row in g["r"]])
+    return g, q, k, v, A, O, r
+
+
+def pin_golden_dense(impl):
+    g, q, k, v, A, O, r = _golden_dense()
+    a = impl.attention_weights(q, k, g["scale"])
+    np.testing.assert_allclose(a, A, rtol=0, atol=1e-15)
+    np.testing.assert_allclose((a @ v)[:, 0], O, rtol=0, atol=1e-14)
+    B = g["block"]
+    for qb in range(r.shape[0]):
+        rows = a[qb * B:(qb + 1) * B]
+        np.testing.assert_allclose(impl.block_mass_rows(rows, B), r[qb], rtol=0, atol=1e-15)
+
+
+def pin_block_mass_sums_to_one(impl):
+    S, D, B = 96, 8, 16
+    q, k, _ = _rand(8, S, D)
+    a = impl.attention_weights(q, k, 0.6)
+    for qb in range(S // B):
+        r = impl.block_mass_rows(a[qb * B:(qb + 1) * B], B)
+        assert abs(r.sum() - 1.0) < 1e-13
+        assert np.all(r[qb + 1:] == 0.0)
+        assert np.all(r[:qb + 1] > 0.0)
+
+
+def pin_block_mass_q_zero_closed_form(impl):
+    """Q = 0: r_qb = (1/B) sum_{i in I_q} |{j in I_b : j <= i}| / (i + 1)."""
+    S, D, B = 64, 4, 8
+    _, k, _ = _rand(9, S, D)
+    a = impl.attention_weights(np.zeros((S, D)), k, 1.0)
+    for qb in range(S // B):
+        r = impl.block_mass_rows(a[qb * B:(qb + 1) * B], B)
+        expect = np.zeros(S // B)
+        for i in range(qb * B, (qb + 1) * B):
+            for b in range(S // B):
+                n_adm = max(0, min(i, (b + 1) * B - 1) - b * B + 1)
+                expect[b] += n_adm / (i + 1)
+        np.testing.assert_allclose(r, expect / B, rtol=0, atol=1e-14)
+
+
+def pin_block_mass_token_level(impl):
+    """B = 1 reduces the block mass to the token attention distribution."""
+    S, D = 17, 3
+    q, k, _ = _rand(10, S, D)
+    a = impl.attention_weights(q, k, 0.8)
+    for i in range(S):
+        np.testing.assert_allclose(impl.block_mass_rows(a[i:i + 1], 1), a[i], rtol=0, atol=1e-15)
+
+
+def pin_block_mass_dominant_key(impl):
+    """One key with a huge logit for every query pulls nearly all mass to its block."""
+    S, D, B = 48, 2, 8
+    g = np.random.default_rng(11)
+    q = np.column_stack([np.ones(S), 0.01 * g.standard_normal(S)])
+    k = 0.01 * g.standard_normal((S, D))
+    k[3, 0] = 60.0                        # key 3 lies in block 0
+    a = impl.attention_weights(q, k, 1.0)
+    for qb in range(1, S // B):
+        r = impl.block_mass_rows(a[qb * B:(qb + 1) * B], B)
+        assert r[0] > 1 - 1e-12 and r[1:].max() < 1e-20 and abs(r.sum() - 1) < 1e-13
+
+
+def _brute_force_support(mbar, q, eta):
+    blocks = list(range(q + 1))
+    for size in range(1, q + 2):
+        feasible = [c for c in itertools.combinations(blocks, size)
+                    if sum(mbar[b] for b in c) >= eta]
+        if feasible:
+            return size, feasible
+    return q + 1, [tuple(blocks)]
+
+
+def pin_selection_brute_force(impl):
+    """Eq. (6): minimum cardinality equals k*, and the chosen set reaches eta."""
+    g = np.random.default_rng(12)
+    for trial in range(60):
+        q = int(g.integers(1, 11))
+        mbar = g.dirichlet(np.full(q + 1, 0.5))
+        eta = float(g.choice([0.5, 0.8, 0.9, 0.95]))
+        got = impl.select_support(mbar, q, eta)
+        size, feasible = _brute_force_support(mbar, q, eta)
+        eta_part = [b for b in got]
+        # the eta-selected blocks are the top-k* by mass (distinct masses here)
+        order = sorted(range(q + 1), key=lambda b: -mbar[b])
+        top = set(order[:size])
+        assert set(got) == top | {0, q}, (trial, got, top)
+        assert sum(mbar[b] for b in top) >= eta
+        assert tuple(sorted(top)) in [tuple(sorted(c)) for c in feasible]
+        assert eta_part == sorted(eta_part)
+
+
+def pin_selection_eta_one_keeps_all(impl):
+    g = np.random.default_rng(13)
+    for q in (0, 1, 5, 30):
+        mbar = g.dirichlet(np.ones(q + 1))
+        assert impl.select_support(mbar, q, 1.0) == list(range(q + 1))
+
+
+def pin_selection_small_eta_keeps_argmax(impl):
+    g = np.random.default_rng(14)
+    for q in (3, 9, 20):
+        mbar = g.dirichlet(np.ones(q + 1))
+        got = impl.select_support(mbar, q, float(mbar.max()) * 0.999)
+        assert got == sorted({int(np.argmax(mbar)), 0, q})
+
+
+def pin_selection_golden(impl):
+    with open(os.path.join(GOLDEN, "selection_dyadic.json")) as f:
+        g = json.load(f)
+    for case in g["cases"]:
+        got = impl.select_support(np.array(case["mbar"]), case["q"], case["eta"], case["cap"])
+        assert got == case["support"], (case, got)
+
+
+def pin_selection_perturbation(impl):
+    """Appendix A.1: a perturbation below Delta_q leaves the support unchanged."""
+    g = np.random.default_rng(15)
+    checked = 0
+    for _ in range(200):
+        q = int(g.integers(2, 25))
+        mbar = g.dirichlet(np.full(q + 1, 0.7))
+        eta = 0.9
+        m = oracle.support_margins(mbar, q, eta)
+        if not (m["Delta"] > 1e-9 and math.isfinite(m["Delta"])):
+            continue
+        base = impl.select_support(mbar, q, eta)
+        for _ in range(5):
+            eps = g.uniform(-1, 1, q + 1) * m["Delta"] * 0.999
+            assert impl.select_support(mbar + eps, q, eta) == base
+        checked += 1
+    assert checked > 50
+
+
+def pin_full_support_reproduces_dense(impl):
+    S, D, B = 64, 8, 16
+    q, k, _ = _rand(16, S, D)
+    sup = {qb: list(range(qb + 1)) for qb in range(S // B)}
+    a_dense = impl.attention_weights(q, k, 0.45)
+    a_mask = impl.masked_attention_weights(q, k, 0.45, B, sup, np.arange(S))
+    assert np.max(np.abs(a_dense - a_mask)) <= 1e-15
+
+
+def pin_diagonal_only_support(impl):
+    """W = {q}: block-local causal attention; with Q = 0 the mean of v over [qB, i]."""
+    S, D, B = 48, 4, 8
+    _, k, v = _rand(17, S, D)
+    sup = {qb: [qb] for qb in range(S // B)}
+    a = impl.masked_attention_weights(np.zeros((S, D)), k, 1.0, B, sup, np.arange(S))
+    o = a @ v
+    for i in range(S):
+        lo = (i // B) * B
+        np.testing.assert_allclose(o[i], v[lo:i + 1].mean(axis=0), rtol=0, atol=1e-13)
+
+
+def pin_sink_and_diagonal_support(impl):
+    S, D, B = 48, 4, 8
+    _, k, v = _rand(18, S, D)
+    sup = {qb: sorted({0, qb}) for qb in range(S // B)}
+    a = impl.masked_attention_weights(np.zeros((S, D)), k, 1.0, B, sup, np.arange(S))
+    o = a @ v
+    for i in range(B, S):
+        lo = (i // B) * B
+        idx = list(range(0, B)) + list(range(lo, i + 1))
+        np.testing.assert_allclose(o[i], v[idx].mean(axis=0), rtol=0, atol=1e-13)
+
+
+def pin_masked_rows_normalised(impl):
+    S, D, B = 64, 5, 8
+    q, k, _ = _rand(19, S, D)
+    g = np.random.default_rng(20)
+    sup = {qb: sorted(set(g.choice(qb + 1, size=min(qb + 1, 3), replace=False).tolist()) | {qb})
+           for qb in range(S // B)}
+    a = impl.masked_attention_weights(q, k, 0.5, B, sup, np.arange(S))
+    np.testing.assert_allclose(a.sum(axis=1), 1.0, rtol=0, atol=1e-13)
+    for i in range(S):
+        allowed = np.zeros(S, dtype=bool)
+        for b in sup[i // B]:
+            allowed[b * B:(b + 1) * B] = True
+        allowed[i + 1:] = False
+        assert np.all(a[i, ~allowed] == 0) and np.all(a[i, allowed] > 0)
+
+
+PINS = [pin_uniform_when_q_zero, pin_constant_values, pin_single_position,
+        pin_logistic_two_keys, pin_causal_rows_sum_to_one, pin_key_shift_invariance,
+        pin_scale_is_a_temperature, pin_golden_dense, pin_block_mass_sums_to_one,
+        pin_block_mass_q_zero_closed_form, pin_block_mass_token_level,
+        pin_block_mass_dominant_key, pin_selection_brute_force,
+        pin_selection_eta_one_keeps_all, pin_selection_small_eta_keeps_argmax,
+        pin_selection_golden, pin_selection_perturbation,
+        pin_full_support_reproduces_dense, pin_diagonal_only_support,
+        pin_sink_and_diagonal_support, pin_masked_rows_normalised]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_oracle_pin(pin):
+    pin(_impl())
+
+
+# --------------------------------------------------------------------------
+# Other pins that do not fit the namespace form
+# --------------------------------------------------------------------------
+
+def test_margins_match_definition():
+    mbar = np.array([0.0625, 0.5, 0.1875, 0.1875, 0.0625])
+    m = oracle.support_margins(mbar, 4, 0.6)
+    assert m["k_star"] == 2
+    assert m["delta_rank"] == 0.0                  # 0.1875 tie at the boundary
+    assert abs(m["delta_minus"] - 0.1) < 1e-15
+    assert abs(m["delta_plus"] - 0.0875) < 1e-15
+
+
+def test_trajectory_dense_only_equals_dense():
+    S, D, B = 64, 8, 16
+    steps = [_rand(30 + t, S, D) for t in range(3)]
+    out = oracle.trajectory_head(steps, td=3, block=B, eta=0.9)
+    for t in range(3):
+        q, k, v = steps[t]
+        np.testing.assert_allclose(out["outputs"][t], oracle.dense_attention(q, k, v),
+                                   rtol=0, atol=0)
+        assert out["mass_sum"].shape == (S // B, S // B)
+
+
+def test_trajectory_eta_one_late_equals_dense():
+    S, D, B = 64, 8, 16
+    steps = [_rand(40 + t, S, D) for t in range(4)]
+    out = oracle.trajectory_head(steps, td=2, block=B, eta=1.0)
+    for qb, sup in out["supports"].items():
+        assert sup == list(range(qb + 1))
+    for t in (2, 3):
+        q, k, v = steps[t]
+        assert np.max(np.abs(out["outputs"][t] - oracle.dense_attention(q, k, v))) <= 1e-15
+    row_sums = out["mass_sum"].sum(axis=1)
+    np.testing.assert_allclose(row_sums, 2.0, rtol=0, atol=1e-13)
+
+
+def test_trajectory_supports_keep_sink_and_diagonal():
+    S, D, B = 128, 8, 16
+    steps = [_rand(50 + t, S, D) for t in range(4)]
+    out = oracle.trajectory_head(steps, td=2, block=B, eta=0.5, cap=1)
+    for qb, sup in out["supports"].items():
+        assert 0 in sup and qb in sup and sup == sorted(sup)
+        assert len(sup) <= 3
+
+
+def test_bf16_widening_exact():
+    bits = np.array([0x3F80, 0xBF80, 0x4049, 0x0000, 0x7F7F], dtype=np.uint16)
+    got = oracle.bf16_to_f64(bits)
+    assert got[0] == 1.0 and got[1] == -1.0 and got[3] == 0.0
+    assert got[2] == 3.140625
+    assert got[4] == float(np.float32(3.3895313892515355e38))
+
+
+# --------------------------------------------------------------------------
+# Mutation tests: each planted mistake must be caught by some pin
+# --------------------------------------------------------------------------
+
+def _caught(impl):
+    for pin in PINS:
+        try:
+            pin(impl)
+        except AssertionError:
+            return True
+    return False
+
+
+def _mut_transposed(q, k, scale, rows=None):
+    S = k.shape[0]
+    r = np.arange(S) if rows is None else np.asarray(rows)
+    s = (k[r] @ q.T) * scale
+    s[np.arange(S)[None, :] > r[:, None]] = -np.inf
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def _mut_no_scale(q, k, scale, rows=None):
+    return oracle.attention_weights(q, k, 1.0, rows)
+
+
+def _mut_mask_off_by_one(q, k, scale, rows=None):
+    S = k.shape[0]
+    r = np.arange(S) if rows is None else np.asarray(rows)
+    s = (q[r] @ k.T) * scale
+    s[np.arange(S)[None, :] >= r[:, None] + 2] = -np.inf      # lets j = i + 1 through
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def _mut_mass_no_norm(a_q, block):
+    return oracle.block_mass_rows(a_q, block) * a_q.shape[0]
+
+
+def _mut_mass_wrong_axis(a_q, block):
+    nb = a_q.shape[1] // block
+    return a_q.reshape(a_q.shape[0], nb, block).sum(axis=(0, 2))[::-1] / a_q.shape[0]
+
+
+def _mut_select_exclusive(mbar, q, eta, cap=0):
+    order = sorted(range(q + 1), key=lambda b: (-float(mbar[b]), b))
+    prefix, k_star = 0.0, q + 1
+    for kk, b in enumerate(order, 1):
+        prefix += float(mbar[b])
+        if prefix > eta:
+            k_star = kk
+            break
+    k = min(k_star, cap) if cap > 0 else k_star
+    return sorted(set(order[:k]) | {0, q})
+
+
+def _mut_select_tie_high(mbar, q, eta, cap=0):
+    order = sorted(range(q + 1), key=lambda b: (-float(mbar[b]), -b))
+    prefix, k_star = 0.0, q + 1
+    for kk, b in enumerate(order, 1):
+        prefix += float(mbar[b])
+        if prefix >= eta:
+            k_star = kk
+            break
+    k = min(k_star, cap) if cap > 0 else k_star
+    return sorted(set(order[:k]) | {0, q})
+
+
+def _mut_select_one_short(mbar, q, eta, cap=0):
+    full = oracle.select_support(mbar, q, eta, cap)
+    order = sorted(range(q + 1), key=lambda b: (-float(mbar[b]), b))
+    prefix, k_star = 0.0, q + 1
+    for kk, b in enumerate(order, 1):
+        prefix += float(mbar[b])
+        if prefix >= eta:
+            k_star = kk
+            break
+    k = max(1, k_star - 1)
+    return sorted(set(order[:k]) | {0, q}) if full else full
+
+
+def _mut_select_no_sink(mbar, q, eta, cap=0):
+    return [b for b in oracle.select_support(mbar, q, eta, cap) if b != 0 or q == 0
+            or b in sorted(range(q + 1), key=lambda c: (-float(mbar[c]), c))[:1]]
+
+
+def _mut_masked_ignores_support(q, k, scale, block, supports, rows):
+    full = {qb: list(range(qb + 1)) for qb in supports}
+    return oracle.masked_attention_weights(q, k, scale, block, full, rows)
+
+
+MUTANTS = {
+    "transposed_operand": dict(attention_weights=_mut_transposed),
+    "missing_scale": dict(attention_weights=_mut_no_scale),
+    "causal_off_by_one": dict(attention_weights=_mut_mask_off_by_one),
+    "mass_missing_1_over_B": dict(block_mass_rows=_mut_mass_no_norm),
+    "mass_wrong_axis": dict(block_mass_rows=_mut_mass_wrong_axis),
+    "select_exclusive_threshold": dict(select_support=_mut_select_exclusive),
+    "select_tie_to_higher_index": dict(select_support=_mut_select_tie_high),
+    "select_one_block_short": dict(select_support=_mut_select_one_short),
+    "select_drops_sink": dict(select_support=_mut_select_no_sink),
+    "masked_ignores_support": dict(masked_attention_weights=_mut_masked_ignores_support),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name):
+    assert _caught(_impl(**MUTANTS[name])), name
