@@ -1,0 +1,249 @@
+"""Python binding of libwise, the WISE working-set attention library (gfx950).
+
+Thin argument marshalling over the C ABI in ``include/wise.h``: every
+function here checks tensor dtypes/shapes/devices, passes raw device
+pointers and the current HIP stream, and turns a non-zero status into
+``WiseError``.  All computation runs in the HIP kernels of ``libwise.so``;
+there is no fallback path.  Build the library with
+``python -m block_sparse_attention_wise_amd.build``.
+
+Layouts (see the header for the full contract):
+  q, k, v, o   bf16  [batch, heads, seq_len, head_dim], contiguous, on the GPU
+  mass         fp32  [batch, heads, n_blocks, n_blocks]
+  row_ptr      int32 [batch * heads * n_blocks + 1]
+  col_idx      int32 [>= wise_select_max_nnz(...)]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = ["WiseError", "WiseDesc", "load_library", "library_path", "wise_full_attn",
+           "wise_full_attn_accum", "wise_select_support", "wise_sparse_attn",
+           "wise_select_max_nnz", "wise_abi_version", "WISE_OK", "WISE_ERR_INVALID_ARG",
+           "WISE_ERR_UNSUPPORTED", "WISE_ERR_CAPACITY", "WISE_ERR_HIP"]
+
+WISE_OK = 0
+WISE_ERR_INVALID_ARG = 1
+WISE_ERR_UNSUPPORTED = 2
+WISE_ERR_CAPACITY = 3
+WISE_ERR_HIP = 4
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.environ.get("WISE_LIBRARY", os.path.join(_HERE, "libwise.so"))
+
+
+class WiseError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        self.status = status
+        super().__init__(f"{func}: status {status} ({_status_name(status)}): {detail}")
+
+
+class WiseDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("seq_len", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libwise.so once; raises if it is missing (no fallback exists)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or library_path()
+    if not os.path.exists(p):
+        raise ImportError(f"libwise.so not found at {p}; build it with "
+                          "`python -m block_sparse_attention_wise_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    dp = ctypes.POINTER(WiseDesc)
+    sigs = {
+        "wise_full_attn": ([dp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+        "wise_full_attn_accum": ([dp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+        "wise_select_support": ([dp, vp, i32, ctypes.c_double, i32, vp, vp, i64, vp], ctypes.c_int),
+        "wise_sparse_attn": ([dp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+        "wise_select_max_nnz": ([dp, i32], i64),
+        "wise_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "wise_last_error": ([], ctypes.c_char_p),
+        "wise_abi_version": ([], i32),
+    }
+    for name, (args, res) in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _status_name(status: int) -> str:
+    return {0: "WISE_OK", 1: "WISE_ERR_INVALID_ARG", 2: "WISE_ERR_UNSUPPORTED",
+            3: "WISE_ERR_CAPACITY", 4: "WISE_ERR_HIP"}.get(status, "?")
+
+
+def _check(status: int, func: str) -> None:
+    if status != WISE_OK:
+        detail = load_library().wise_last_error().decode(errors="replace")
+        raise WiseError(status, func, detail)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _need(t, name, dtype, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def _desc(q, block_size: int, softmax_scale: float) -> WiseDesc:
+    b, h, s, d = q.shape
+    return WiseDesc(b, h, s, d, int(block_size), float(softmax_scale))
+
+
+def _qkv(q, k, v):
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, 4)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"q/k/v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
+
+
+def _out(o, q):
+    torch = _torch()
+    if o is None:
+        return torch.empty_like(q)
+    _need(o, "o", torch.bfloat16, 4)
+    if o.shape != q.shape:
+        raise ValueError("o must have q's shape")
+    return o
+
+
+def wise_full_attn(q, k, v, block_size: int, o=None, lse=None, softmax_scale: float = 0.0,
+                   stream=None):
+    """Dense causal attention (Eq. 2).  Returns o (bf16)."""
+    torch = _torch()
+    _qkv(q, k, v)
+    o = _out(o, q)
+    lse_ptr = None
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 3)
+        if tuple(lse.shape) != tuple(q.shape[:3]):
+            raise ValueError("lse must be [batch, heads, seq_len]")
+        lse_ptr = lse.data_ptr()
+    d = _desc(q, block_size, softmax_scale)
+    st = load_library().wise_full_attn(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                       o.data_ptr(), lse_ptr, _stream_ptr(stream))
+    _check(st, "wise_full_attn")
+    return o
+
+
+def _mass_shape(q, block_size):
+    b, h, s, _ = q.shape
+    nb = s // block_size
+    return (b, h, nb, nb)
+
+
+def wise_full_attn_accum(q, k, v, mass, block_size: int, o=None, softmax_scale: float = 0.0,
+                         stream=None):
+    """Discovery step: dense attention + block mass (Eq. 2, 5) added into ``mass``."""
+    torch = _torch()
+    _qkv(q, k, v)
+    _need(mass, "mass", torch.float32, 4)
+    if tuple(mass.shape) != _mass_shape(q, block_size):
+        raise ValueError(f"mass must be {_mass_shape(q, block_size)}, got {tuple(mass.shape)}")
+    o = _out(o, q)
+    d = _desc(q, block_size, softmax_scale)
+    st = load_library().wise_full_attn_accum(ctypes.byref(d), q.data_ptr(), k.data_ptr(),
+                                             v.data_ptr(), o.data_ptr(), mass.data_ptr(),
+                                             _stream_ptr(stream))
+    _check(st, "wise_full_attn_accum")
+    return o
+
+
+def wise_select_max_nnz(batch: int, heads: int, seq_len: int, head_dim: int, block_size: int,
+                        max_blocks: int = 0) -> int:
+    d = WiseDesc(batch, heads, seq_len, head_dim, block_size, 0.0)
+    n = load_library().wise_select_max_nnz(ctypes.byref(d), int(max_blocks))
+    if n < 0:
+        raise WiseError(WISE_ERR_INVALID_ARG, "wise_select_max_nnz", "invalid shape")
+    return int(n)
+
+
+def wise_select_support(mass, n_steps: int, eta: float, head_dim: int, block_size: int,
+                        max_blocks: int = 0, row_ptr=None, col_idx=None,
+                        stream=None) -> Tuple[object, object]:
+    """Working-set selection (Eq. 6 + sink/diagonal) -> (row_ptr, col_idx) CSR.
+
+    ``col_idx`` is sized to the worst case; its first ``row_ptr[-1]`` entries
+    are meaningful.
+    """
+    torch = _torch()
+    _need(mass, "mass", torch.float32, 4)
+    b, h, nb, nb2 = mass.shape
+    if nb != nb2:
+        raise ValueError("mass must be [batch, heads, n_blocks, n_blocks]")
+    seq = nb * block_size
+    d = WiseDesc(b, h, seq, head_dim, block_size, 0.0)
+    cap = wise_select_max_nnz(b, h, seq, head_dim, block_size, max_blocks)
+    n_rows = b * h * nb
+    if row_ptr is None:
+        row_ptr = torch.empty(n_rows + 1, dtype=torch.int32, device=mass.device)
+    if col_idx is None:
+        col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=mass.device)
+    _need(row_ptr, "row_ptr", torch.int32, 1)
+    _need(col_idx, "col_idx", torch.int32, 1)
+    if row_ptr.numel() != n_rows + 1:
+        raise ValueError(f"row_ptr must have {n_rows + 1} entries")
+    st = load_library().wise_select_support(ctypes.byref(d), mass.data_ptr(), int(n_steps),
+                                            float(eta), int(max_blocks), row_ptr.data_ptr(),
+                                            col_idx.data_ptr(), col_idx.numel(),
+                                            _stream_ptr(stream))
+    _check(st, "wise_select_support")
+    return row_ptr, col_idx
+
+
+def wise_sparse_attn(q, k, v, row_ptr, col_idx, block_size: int, o=None,
+                     softmax_scale: float = 0.0, stream=None):
+    """Reuse step: attention restricted to the CSR block support (Eq. 7-8)."""
+    torch = _torch()
+    _qkv(q, k, v)
+    _need(row_ptr, "row_ptr", torch.int32, 1)
+    _need(col_idx, "col_idx", torch.int32, 1)
+    b, h, s, _ = q.shape
+    if row_ptr.numel() != b * h * (s // block_size) + 1:
+        raise ValueError("row_ptr must have batch*heads*n_blocks + 1 entries")
+    o = _out(o, q)
+    d = _desc(q, block_size, softmax_scale)
+    st = load_library().wise_sparse_attn(ctypes.byref(d), q.data_ptr(), k.data_ptr(),
+                                         v.data_ptr(), row_ptr.data_ptr(), col_idx.data_ptr(),
+                                         o.data_ptr(), _stream_ptr(stream))
+    _check(st, "wise_sparse_attn")
+    return o
+
+
+def wise_abi_version() -> int:
+    return int(load_library().wise_abi_version())

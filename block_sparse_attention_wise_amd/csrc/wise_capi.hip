@@ -1,0 +1,224 @@
+// C ABI of libwise (declared in include/wise.h): host-side validation and
+// dispatch to the HIP kernels.  Validation is pure host code and touches no
+// device state, so invalid calls return before anything is launched.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/wise.h"
+#include "wise_internal.h"
+
+namespace wise {
+
+size_t attn_lds_bytes_d64(int block, int mode, int nblk);
+size_t attn_lds_bytes_d96(int block, int mode, int nblk);
+size_t attn_lds_bytes_d128(int block, int mode, int nblk);
+
+size_t attn_lds_bytes(int head_dim, int block, int mode, int nblk) {
+  switch (head_dim) {
+    case 64: return attn_lds_bytes_d64(block, mode, nblk);
+    case 96: return attn_lds_bytes_d96(block, mode, nblk);
+    case 128: return attn_lds_bytes_d128(block, mode, nblk);
+  }
+  return 0;
+}
+
+hipError_t launch_attn(const AttnLaunch& cfg, const AttnParams& p, hipStream_t stream) {
+  switch (cfg.head_dim) {
+    case 64: return launch_attn_d64(cfg.block, cfg.mode, p, stream);
+    case 96: return launch_attn_d96(cfg.block, cfg.mode, p, stream);
+    case 128: return launch_attn_d128(cfg.block, cfg.mode, p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+wise_status_t fail(wise_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+wise_status_t fail(wise_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+wise_status_t ok() {
+  g_last_error[0] = '\0';
+  return WISE_OK;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// Shape checks common to every call.  Fills nblk / n_rows on success.
+wise_status_t check_desc(const wise_attn_desc_t* d, int32_t* nblk, int64_t* n_rows) {
+  if (d == nullptr) return fail(WISE_ERR_INVALID_ARG, "desc is NULL");
+  if (d->batch < 1 || d->heads < 1)
+    return fail(WISE_ERR_INVALID_ARG, "batch (%d) and heads (%d) must be >= 1", d->batch, d->heads);
+  if (d->block_size != 32 && d->block_size != 64 && d->block_size != 128)
+    return fail(WISE_ERR_UNSUPPORTED, "block_size %d not built (32, 64, 128)", d->block_size);
+  if (d->head_dim != 64 && d->head_dim != 96 && d->head_dim != 128)
+    return fail(WISE_ERR_UNSUPPORTED, "head_dim %d not built (64, 96, 128)", d->head_dim);
+  if (d->seq_len < d->block_size || d->seq_len % d->block_size != 0)
+    return fail(WISE_ERR_INVALID_ARG, "seq_len %d must be a positive multiple of block_size %d",
+                d->seq_len, d->block_size);
+  if (d->seq_len > 65536)
+    return fail(WISE_ERR_UNSUPPORTED, "seq_len %d above 65536", d->seq_len);
+  if (!std::isfinite(d->softmax_scale))
+    return fail(WISE_ERR_INVALID_ARG, "softmax_scale is not finite");
+  const int64_t heads_total = (int64_t)d->batch * d->heads;
+  const int64_t rows = heads_total * (d->seq_len / d->block_size);
+  if (rows >= (int64_t)INT32_MAX)
+    return fail(WISE_ERR_UNSUPPORTED, "batch*heads*n_blocks = %lld too large", (long long)rows);
+  *nblk = d->seq_len / d->block_size;
+  *n_rows = rows;
+  return WISE_OK;
+}
+
+wise_status_t check_tensor(const void* ptr, const char* name) {
+  if (ptr == nullptr) return fail(WISE_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(ptr)) return fail(WISE_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return WISE_OK;
+}
+
+float scale_log2(const wise_attn_desc_t* d) {
+  const double s = d->softmax_scale > 0.f ? (double)d->softmax_scale : 1.0 / std::sqrt((double)d->head_dim);
+  return (float)(s * 1.4426950408889634);  // log2(e)
+}
+
+wise_status_t run_attn(const wise_attn_desc_t* d, int mode, const void* q, const void* k, const void* v,
+                       void* o, float* lse, float* mass, const int32_t* row_ptr, const int32_t* col_idx,
+                       void* stream) {
+  int32_t nblk;
+  int64_t n_rows;
+  wise_status_t st = check_desc(d, &nblk, &n_rows);
+  if (st != WISE_OK) return st;
+  if ((st = check_tensor(q, "q")) != WISE_OK) return st;
+  if ((st = check_tensor(k, "k")) != WISE_OK) return st;
+  if ((st = check_tensor(v, "v")) != WISE_OK) return st;
+  if ((st = check_tensor(o, "o")) != WISE_OK) return st;
+  if (o == q || o == k || o == v) return fail(WISE_ERR_INVALID_ARG, "o aliases an input");
+  if (mode == kDenseMass && mass == nullptr) return fail(WISE_ERR_INVALID_ARG, "mass is NULL");
+  if (mode == kSparse && (row_ptr == nullptr || col_idx == nullptr))
+    return fail(WISE_ERR_INVALID_ARG, "row_ptr / col_idx is NULL");
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(WISE_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+  if (mass != nullptr && (reinterpret_cast<uintptr_t>(mass) & 3u))
+    return fail(WISE_ERR_INVALID_ARG, "mass is not 4-byte aligned");
+  const size_t lds = attn_lds_bytes(d->head_dim, d->block_size, mode, nblk);
+  if (lds == 0 || lds > kMaxLds)
+    return fail(WISE_ERR_UNSUPPORTED, "seq_len %d needs %zu B of LDS for this call", d->seq_len, lds);
+
+  AttnParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.mass = mass;
+  p.row_ptr = row_ptr;
+  p.col_idx = col_idx;
+  p.heads_total = d->batch * d->heads;
+  p.seq = d->seq_len;
+  p.nblk = nblk;
+  p.scale_log2 = scale_log2(d);
+  AttnLaunch cfg{d->head_dim, d->block_size, mode};
+  const hipError_t e = launch_attn(cfg, p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(WISE_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int64_t max_nnz(int32_t nblk, int64_t heads_total, int32_t max_blocks) {
+  int64_t per_head = 0;
+  for (int32_t q = 0; q < nblk; ++q) {
+    int64_t n = q + 1;
+    if (max_blocks > 0 && n > (int64_t)max_blocks + 2) n = (int64_t)max_blocks + 2;
+    per_head += n;
+  }
+  return per_head * heads_total;
+}
+
+}  // namespace
+}  // namespace wise
+
+using namespace wise;
+
+extern "C" {
+
+wise_status_t wise_full_attn(const wise_attn_desc_t* desc, const void* q, const void* k, const void* v,
+                             void* o, float* lse, void* stream) {
+  return run_attn(desc, kDense, q, k, v, o, lse, nullptr, nullptr, nullptr, stream);
+}
+
+wise_status_t wise_full_attn_accum(const wise_attn_desc_t* desc, const void* q, const void* k,
+                                   const void* v, void* o, float* mass, void* stream) {
+  return run_attn(desc, kDenseMass, q, k, v, o, nullptr, mass, nullptr, nullptr, stream);
+}
+
+wise_status_t wise_sparse_attn(const wise_attn_desc_t* desc, const void* q, const void* k, const void* v,
+                               const int32_t* row_ptr, const int32_t* col_idx, void* o, void* stream) {
+  return run_attn(desc, kSparse, q, k, v, o, nullptr, nullptr, row_ptr, col_idx, stream);
+}
+
+int64_t wise_select_max_nnz(const wise_attn_desc_t* desc, int32_t max_blocks) {
+  int32_t nblk;
+  int64_t n_rows;
+  if (check_desc(desc, &nblk, &n_rows) != WISE_OK || max_blocks < 0) return -1;
+  return max_nnz(nblk, (int64_t)desc->batch * desc->heads, max_blocks);
+}
+
+wise_status_t wise_select_support(const wise_attn_desc_t* desc, const float* mass, int32_t n_steps,
+                                  double eta, int32_t max_blocks, int32_t* row_ptr, int32_t* col_idx,
+                                  int64_t col_capacity, void* stream) {
+  int32_t nblk;
+  int64_t n_rows;
+  wise_status_t st = check_desc(desc, &nblk, &n_rows);
+  if (st != WISE_OK) return st;
+  if (mass == nullptr || row_ptr == nullptr || col_idx == nullptr)
+    return fail(WISE_ERR_INVALID_ARG, "mass / row_ptr / col_idx is NULL");
+  if ((reinterpret_cast<uintptr_t>(mass) | reinterpret_cast<uintptr_t>(row_ptr) |
+       reinterpret_cast<uintptr_t>(col_idx)) & 3u)
+    return fail(WISE_ERR_INVALID_ARG, "mass / row_ptr / col_idx not 4-byte aligned");
+  if (n_steps < 1) return fail(WISE_ERR_INVALID_ARG, "n_steps %d must be >= 1", n_steps);
+  if (!(eta > 0.0 && eta <= 1.0)) return fail(WISE_ERR_INVALID_ARG, "eta %g outside (0, 1]", eta);
+  if (max_blocks < 0) return fail(WISE_ERR_INVALID_ARG, "max_blocks %d < 0", max_blocks);
+  if (nblk > 64 * 32) return fail(WISE_ERR_UNSUPPORTED, "n_blocks %d above 2048", nblk);
+  const int64_t need = max_nnz(nblk, (int64_t)desc->batch * desc->heads, max_blocks);
+  if (need >= (int64_t)INT32_MAX)
+    return fail(WISE_ERR_UNSUPPORTED, "worst-case nnz %lld does not fit int32", (long long)need);
+  if (col_capacity < need)
+    return fail(WISE_ERR_CAPACITY, "col_capacity %lld below worst-case nnz %lld", (long long)col_capacity,
+                (long long)need);
+  SelectParams p{};
+  p.mass = mass;
+  p.row_ptr = row_ptr;
+  p.col_idx = col_idx;
+  p.n_rows = (int32_t)n_rows;
+  p.nblk = nblk;
+  p.max_blocks = max_blocks;
+  p.n_steps = (double)n_steps;
+  p.eta = eta;
+  const hipError_t e = launch_select(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(WISE_ERR_HIP, "selection launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* wise_status_string(wise_status_t status) {
+  switch (status) {
+    case WISE_OK: return "WISE_OK";
+    case WISE_ERR_INVALID_ARG: return "WISE_ERR_INVALID_ARG";
+    case WISE_ERR_UNSUPPORTED: return "WISE_ERR_UNSUPPORTED";
+    case WISE_ERR_CAPACITY: return "WISE_ERR_CAPACITY";
+    case WISE_ERR_HIP: return "WISE_ERR_HIP";
+  }
+  return "WISE_ERR_UNKNOWN";
+}
+
+const char* wise_last_error(void) { return g_last_error; }
+
+int32_t wise_abi_version(void) { return WISE_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Internal declarations shared by the HIP translation units of libwise.
+// Not part of the public interface (that is include/wise.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wise {
+
+// Kinds of attention launch: the same kernel body serves all three.
+enum AttnMode : int {
+  kDense = 0,      // Eq. (2) over every admissible key block
+  kDenseMass = 1,  // Eq. (2) plus the block mass of Eq. (5), added into `mass`
+  kSparse = 2      // Eq. (8): only the key blocks listed in the CSR row
+};
+
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;              // optional, kDense only
+  float* mass;             // kDenseMass only
+  const int32_t* row_ptr;  // kSparse only
+  const int32_t* col_idx;  // kSparse only
+  int32_t heads_total;     // batch * heads
+  int32_t seq;
+  int32_t nblk;            // seq / block
+  float scale_log2;        // softmax scale * log2(e)
+};
+
+struct AttnLaunch {
+  int head_dim;
+  int block;
+  int mode;
+};
+
+// Bytes of dynamic LDS a launch needs (0 if the shape is not built).
+size_t attn_lds_bytes(int head_dim, int block, int mode, int nblk);
+
+// Launch one attention pass over all rows; returns hipSuccess or the error.
+hipError_t launch_attn(const AttnLaunch& cfg, const AttnParams& p, hipStream_t stream);
+
+// Per-D launchers (one translation unit each).
+hipError_t launch_attn_d64(int block, int mode, const AttnParams& p, hipStream_t stream);
+hipError_t launch_attn_d96(int block, int mode, const AttnParams& p, hipStream_t stream);
+hipError_t launch_attn_d128(int block, int mode, const AttnParams& p, hipStream_t stream);
+
+struct SelectParams {
+  const float* mass;
+  int32_t* row_ptr;
+  int32_t* col_idx;
+  int32_t n_rows;
+  int32_t nblk;
+  int32_t max_blocks;  // 0 = no cap
+  double n_steps;      // discovery steps summed into mass
+  double eta;
+};
+
+hipError_t launch_select(const SelectParams& p, hipStream_t stream);
+
+// LDS budget of one workgroup on gfx950.
+constexpr size_t kMaxLds = 160 * 1024;
+
+}  // namespace wise

@@ -1,0 +1,154 @@
+/*
+ * wise.h - C ABI of the WISE working-set attention library (gfx950 / MI355X).
+ *
+ * WISE ("Attention Routing Stabilizes Early: Working-Set Inference for
+ * Recurrent Language Models") runs unrestricted causal attention during the
+ * first td recurrent steps, measures how much attention each query block
+ * sends to each key block, turns that into a block support once, and then
+ * recomputes attention only inside that support in the remaining steps.
+ * This library provides the four device operations of that path:
+ *
+ *   wise_full_attn        dense causal attention (Section 3, Eq. 2)
+ *   wise_full_attn_accum  dense causal attention + block mass (Eq. 2 and 5)
+ *   wise_select_support   mass -> CSR block support (Section 5.1, Eq. 6)
+ *   wise_sparse_attn      attention inside the support (Section 5.2, Eq. 7-8)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Tensors are device pointers owned by the caller; the library allocates
+ *   no device memory and keeps no state between calls.
+ * - Q, K, V, O are bf16 (raw 16-bit patterns), contiguous, laid out
+ *   [batch][heads][seq_len][head_dim].  Q, K and V are read-only; O may not
+ *   alias them.  All pointers must be 16-byte aligned.
+ * - Attention is causal: key j is admissible for query i iff j <= i (the
+ *   mask M of Eq. 2).  Scores are (q_i . k_j) * scale, scale = 1/sqrt(head_dim)
+ *   unless desc->softmax_scale > 0.
+ * - The sequence is cut into blocks of block_size positions (Section 5.1);
+ *   n_blocks = seq_len / block_size, and seq_len must be a multiple of
+ *   block_size.  A "row" is one (batch, head, query block) triple, numbered
+ *   r = (b * heads + h) * n_blocks + q; there are batch*heads*n_blocks rows.
+ * - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *   stream) and never synchronises the host.  Arguments are validated on the
+ *   host first: on any error nothing is launched and nothing is written.
+ * - Results are deterministic: identical inputs give bitwise identical
+ *   outputs (no atomics on any value path).
+ * - No C++ exception crosses this interface.  The library is thread-safe.
+ *
+ * Supported shapes: head_dim in {64, 96, 128}; block_size in {32, 64, 128};
+ * seq_len <= 65536; batch*heads*n_blocks < 2^31.
+ */
+#ifndef WISE_H
+#define WISE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WISE_ABI_VERSION 1
+
+typedef enum {
+  WISE_OK = 0,
+  WISE_ERR_INVALID_ARG = 1,  /* null pointer, bad size, eta outside (0,1], ... */
+  WISE_ERR_UNSUPPORTED = 2,  /* valid but not built: head_dim or block_size    */
+  WISE_ERR_CAPACITY = 3,     /* col_capacity below wise_select_max_nnz()       */
+  WISE_ERR_HIP = 4           /* the HIP runtime reported a launch error        */
+} wise_status_t;
+
+/* Shape of one attention call.  All tensors of a call share it. */
+typedef struct {
+  int32_t batch;       /* >= 1                                         */
+  int32_t heads;       /* >= 1; Q, K and V have the same head count    */
+  int32_t seq_len;     /* >= block_size, multiple of block_size         */
+  int32_t head_dim;    /* 64, 96 or 128                                 */
+  int32_t block_size;  /* B of Section 5.1: 32, 64 or 128               */
+  float softmax_scale; /* <= 0 selects 1/sqrt(head_dim)                 */
+} wise_attn_desc_t;
+
+/*
+ * Dense causal attention, Eq. (2): O = softmax(Q K^T * scale + M) V.
+ *
+ * q, k, v: bf16 [batch][heads][seq_len][head_dim] (read).
+ * o:       bf16, same layout (written, rounded to nearest even).
+ * lse:     optional (NULL to skip) fp32 [batch][heads][seq_len]; receives
+ *          the natural-log row normaliser log(sum_j exp(score_ij)).
+ * This is the dense baseline that the late steps are compared against.
+ */
+wise_status_t wise_full_attn(const wise_attn_desc_t* desc, const void* q, const void* k,
+                             const void* v, void* o, float* lse, void* stream);
+
+/*
+ * Discovery step: dense causal attention (Eq. 2) plus the block mass of
+ * Section 5.1, Eq. (5), r_qb = (1/B) sum_{i in I_q} sum_{j in I_b, j<=i} A_ij,
+ * added in place:  mass[b][h][q][kb] += r_qb  for kb <= q.
+ *
+ * q, k, v, o: as in wise_full_attn.
+ * mass: fp32 [batch][heads][n_blocks][n_blocks], read-modify-written.  The
+ *       caller zeroes it before the first discovery step; calling once per
+ *       discovery step leaves the sum of r over those steps.  Entries with
+ *       kb > q are never touched.  The mass reduction is fused into the
+ *       attention kernel (no second pass over the attention matrix).
+ */
+wise_status_t wise_full_attn_accum(const wise_attn_desc_t* desc, const void* q, const void* k,
+                                   const void* v, void* o, float* mass, void* stream);
+
+/*
+ * Working-set selection, Section 5.1, Eq. (6) (Appendix A.1, Eq. 12), once
+ * after discovery.  For every row (b, h, q), with mbar_kb = mass[..][kb] /
+ * n_steps for the admissible blocks kb = 0..q:
+ *   1. rank blocks by mbar descending, ties by lower block index;
+ *   2. k* = smallest k whose k leading masses sum to >= eta (float64 sums;
+ *      all blocks if the total stays below eta);
+ *   3. k  = min(k*, max_blocks) when max_blocks > 0;
+ *   4. W  = the k leading blocks, plus the sink block 0 and the diagonal
+ *      block q (these two do not count toward eta or the cap).
+ * Output is a CSR over rows, column indices ascending within each row:
+ *   row_ptr: int32 [n_rows + 1] (written; row_ptr[n_rows] = total nnz),
+ *   col_idx: int32 [col_capacity] (the first row_ptr[n_rows] entries written).
+ *
+ * mass: fp32 [batch][heads][n_blocks][n_blocks] (read; entries kb > q ignored).
+ * n_steps >= 1; eta in (0, 1]; max_blocks >= 0 (0 = no cap).
+ * col_capacity must be >= wise_select_max_nnz(desc, max_blocks), else
+ * WISE_ERR_CAPACITY is returned before any launch.
+ */
+wise_status_t wise_select_support(const wise_attn_desc_t* desc, const float* mass,
+                                  int32_t n_steps, double eta, int32_t max_blocks,
+                                  int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                                  void* stream);
+
+/*
+ * Reuse step, Section 5.2, Eq. (7)-(8): O = softmax(Q K^T * scale + M + R) V,
+ * where R_ij = 0 if key block b(j) is listed in the CSR row of query block
+ * q(i) and -inf otherwise.  Only the listed key blocks are read and computed;
+ * the causal mask applies inside the diagonal block.
+ *
+ * q, k, v, o: as in wise_full_attn.
+ * row_ptr, col_idx: CSR over rows (as written by wise_select_support).  Each
+ *          row must list distinct blocks in ascending order, all <= q.  A row
+ *          whose listed blocks hold no admissible key for some query yields
+ *          zeros for that query.
+ */
+wise_status_t wise_sparse_attn(const wise_attn_desc_t* desc, const void* q, const void* k,
+                               const void* v, const int32_t* row_ptr, const int32_t* col_idx,
+                               void* o, void* stream);
+
+/* Upper bound of the CSR size wise_select_support can write:
+ * sum over rows of min(q + 1, max_blocks + 2) (q + 1 when max_blocks == 0).
+ * Returns -1 for an invalid descriptor. */
+int64_t wise_select_max_nnz(const wise_attn_desc_t* desc, int32_t max_blocks);
+
+/* Static, human-readable name of a status code. */
+const char* wise_status_string(wise_status_t status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* wise_last_error(void);
+
+/* WISE_ABI_VERSION of the built library. */
+int32_t wise_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WISE_H */

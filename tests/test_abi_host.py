@@ -1,0 +1,133 @@
+"""Host-only checks of the C ABI: the library loads, exports every function the
+header declares, and rejects invalid arguments before touching the device.
+
+No call here passes validation, so nothing is ever launched (these tests run
+without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_wise_amd as wise
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wise.h")
+
+FAKE = 0x10000        # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+def _lib():
+    if not os.path.exists(wise.library_path()):
+        pytest.skip("libwise.so not built")
+    return wise.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(wise_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_expected_calls():
+    names = _declared_functions()
+    for n in ("wise_full_attn", "wise_full_attn_accum", "wise_select_support", "wise_sparse_attn",
+              "wise_select_max_nnz", "wise_status_string", "wise_last_error", "wise_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings():
+    lib = _lib()
+    assert lib.wise_abi_version() == 1
+    assert lib.wise_status_string(0) == b"WISE_OK"
+    assert lib.wise_status_string(3) == b"WISE_ERR_CAPACITY"
+    assert lib.wise_status_string(99) == b"WISE_ERR_UNKNOWN"
+
+
+def _desc(b=1, h=2, s=256, d=64, blk=32, scale=0.0):
+    return wise.WiseDesc(b, h, s, d, blk, scale)
+
+
+@pytest.mark.parametrize("nb,cap", [(8, 0), (8, 2), (64, 0), (64, 10), (1, 0)])
+def test_select_max_nnz_closed_form(nb, cap):
+    _lib()
+    blk = 32
+    per_head = sum(min(q + 1, cap + 2) if cap > 0 else q + 1 for q in range(nb))
+    assert wise.wise_select_max_nnz(2, 3, nb * blk, 64, blk, cap) == 6 * per_head
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_invalid_descriptors_rejected():
+    lib = _lib()
+    f = lib.wise_full_attn
+    assert f(None, FAKE, FAKE, FAKE, FAKE + 4096, None, None) == wise.WISE_ERR_INVALID_ARG
+    for d, want in [(_desc(b=0), wise.WISE_ERR_INVALID_ARG), (_desc(h=-1), wise.WISE_ERR_INVALID_ARG),
+                    (_desc(d=80), wise.WISE_ERR_UNSUPPORTED), (_desc(blk=48), wise.WISE_ERR_UNSUPPORTED),
+                    (_desc(s=250), wise.WISE_ERR_INVALID_ARG), (_desc(s=16), wise.WISE_ERR_INVALID_ARG),
+                    (_desc(s=131072), wise.WISE_ERR_UNSUPPORTED),
+                    (_desc(scale=float("nan")), wise.WISE_ERR_INVALID_ARG)]:
+        # bad desc, null o: the desc check must fire first or the pointer check; either way no launch
+        st = f(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, None)
+        assert st == want, (d.batch, d.heads, d.seq_len, d.head_dim, d.block_size, st)
+        assert lib.wise_last_error() != b""
+
+
+def test_invalid_pointers_rejected():
+    lib = _lib()
+    d = _desc()
+    f = lib.wise_full_attn
+    assert f(ctypes.byref(d), None, FAKE, FAKE, FAKE + 4096, None, None) == wise.WISE_ERR_INVALID_ARG
+    assert f(ctypes.byref(d), FAKE + 2, FAKE, FAKE, FAKE + 4096, None, None) == wise.WISE_ERR_INVALID_ARG
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None) == wise.WISE_ERR_INVALID_ARG  # o aliases q
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE + 4096, FAKE + 4098, None) == wise.WISE_ERR_INVALID_ARG
+    assert lib.wise_full_attn_accum(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE + 4096, None, None) \
+        == wise.WISE_ERR_INVALID_ARG
+    assert lib.wise_sparse_attn(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, FAKE + 4096, None) \
+        == wise.WISE_ERR_INVALID_ARG
+    assert lib.wise_sparse_attn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE + 4096, None) \
+        == wise.WISE_ERR_INVALID_ARG
+
+
+def test_select_arguments_rejected():
+    lib = _lib()
+    d = _desc(s=256, blk=32)
+    sel = lib.wise_select_support
+    need = lib.wise_select_max_nnz(ctypes.byref(d), 0)
+    assert need == 2 * sum(range(1, 9))
+    # eta outside (0, 1]
+    for eta in (0.0, -0.5, 1.0000001, float("nan")):
+        assert sel(ctypes.byref(d), FAKE, 2, eta, 0, FAKE, FAKE, need, None) == wise.WISE_ERR_INVALID_ARG
+    assert sel(ctypes.byref(d), FAKE, 0, 0.9, 0, FAKE, FAKE, need, None) == wise.WISE_ERR_INVALID_ARG
+    assert sel(ctypes.byref(d), FAKE, 2, 0.9, -1, FAKE, FAKE, need, None) == wise.WISE_ERR_INVALID_ARG
+    assert sel(ctypes.byref(d), None, 2, 0.9, 0, FAKE, FAKE, need, None) == wise.WISE_ERR_INVALID_ARG
+    assert sel(ctypes.byref(d), FAKE + 2, 2, 0.9, 0, FAKE, FAKE, need, None) == wise.WISE_ERR_INVALID_ARG
+    # capacity below the worst case is refused before any launch
+    assert sel(ctypes.byref(d), FAKE, 2, 0.9, 0, FAKE, FAKE, need - 1, None) == wise.WISE_ERR_CAPACITY
+    capped = lib.wise_select_max_nnz(ctypes.byref(d), 1)
+    assert capped == 2 * sum(min(q + 1, 3) for q in range(8))
+    assert sel(ctypes.byref(d), FAKE, 2, 0.9, 1, FAKE, FAKE, capped - 1, None) == wise.WISE_ERR_CAPACITY
+    assert lib.wise_select_max_nnz(None, 0) == -1
+    assert lib.wise_select_max_nnz(ctypes.byref(d), -3) == -1
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    _lib()
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        wise.wise_full_attn(q, q, q, 32)
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(wise, "_lib", None)
+    with pytest.raises(ImportError):
+        wise.load_library(str(tmp_path / "missing.so"))
