@@ -1,0 +1,338 @@
+"""Benchmark of the WISE working-set attention path on one MI355X.
+
+One timed step is one whole recurrent-attention trajectory of the 4K
+workload (batch 1, 32 heads, head_dim 128, seq 4096, block 64, T = 32
+recurrent steps, td = 8, eta = 0.9): td discovery steps (dense attention +
+fused block mass), one support selection, and T - td reuse steps of
+block-sparse attention, each step on its own synthetic Q/K/V already resident
+in HBM.  The headline value is the late-step block-sparse kernel's throughput
+on its executed MFMA FLOPs; the same run reports the late-step speedup over
+the library's own dense kernel, the realised support density, a roofline
+record for the sparse kernel and the fp64 CPU oracle timed on a sample.
+
+    python bench.py [--steps K] [--warmup W] [--config ctx4k] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "late-step sparse-attn TFLOP/s (% bf16 MFMA peak) + speedup vs dense, 4K ctx"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="ctx4k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="run a plain device copy of MIB MiB first (HBM counter calibration)")
+    ap.add_argument("--same-backend", action="store_true",
+                    help="also time the sparse kernel on a full causal CSR")
+    return ap.parse_args(argv)
+
+
+def flop_counts(cfg, row_ptr_h):
+    """Executed and algorithmic FLOPs of one sparse launch and one dense launch."""
+    B, D, nb = cfg.block, cfg.head_dim, cfg.n_blocks
+    heads = cfg.batch * cfg.heads
+    n_rows = heads * nb
+    nnz = int(row_ptr_h[-1])
+    sparse_exec = 4.0 * D * B * B * nnz
+    # every row holds its diagonal block, of which B(B+1)/2 query-key pairs are admissible
+    sparse_alg = 4.0 * D * (B * B * (nnz - n_rows) + n_rows * B * (B + 1) / 2)
+    dense_blocks = heads * nb * (nb + 1) // 2
+    dense_exec = 4.0 * D * B * B * dense_blocks
+    dense_alg = 4.0 * D * heads * cfg.seq_len * (cfg.seq_len + 1) / 2
+    return dict(nnz=nnz, n_rows=n_rows, sparse_exec=sparse_exec, sparse_alg=sparse_alg,
+                dense_exec=dense_exec, dense_alg=dense_alg, dense_blocks=dense_blocks,
+                density_adm=nnz / dense_blocks, density_full=nnz / (heads * nb * nb))
+
+
+def sparse_bytes(cfg, nnz, n_rows):
+    """Compulsory HBM bytes of one sparse launch: Q, K, V read once, O written
+    once (8 * S * D bytes per head), plus the CSR.  Re-reads of a K/V block by
+    several rows are meant to hit L2/MALL."""
+    D = cfg.head_dim
+    heads = cfg.batch * cfg.heads
+    qkvo = 4 * 2.0 * heads * cfg.seq_len * D
+    csr = 4.0 * (n_rows + 1 + nnz)
+    return qkvo + csr
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_ctx4k_hbm_traffic.md")
+KERNEL_SOURCES = ["block_sparse_attention_wise_amd/csrc/wise_attn_kernel.h",
+                  "block_sparse_attention_wise_amd/csrc/wise_attn_d128.hip"]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per sparse launch from the committed rocprofv3 counter runs
+    (FETCH_SIZE / WRITE_SIZE, copy-calibrated), or None when the attention
+    kernel source changed since they were taken."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if ":" in line and line.split(":")[0].strip() in (
+                        "kernel_source_hash", "sparse_read_bytes_per_launch",
+                        "sparse_write_bytes_per_launch"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_hash") != kernel_source_hash():
+            return None
+        return int(kv["sparse_read_bytes_per_launch"]) + int(kv["sparse_write_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(cfg, n_heads: int):
+    """The fp64 oracle, as it stands, on a bounded sample: the first
+    ``n_heads`` heads of the workload, each through td dense steps, the
+    selection and all T - td late steps.  Only the late steps are timed; the
+    rate uses the same algorithmic FLOP count as the GPU figure, restricted to
+    the sample."""
+    import oracle
+    from wise_inputs import Workload
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:                                          # pragma: no cover
+        threads = os.cpu_count() or 1
+    wl = Workload(cfg, threads=1)
+    B, td = cfg.block, cfg.td
+    sc = oracle.default_scale(cfg.head_dim)
+    t_late, flops, n_late = 0.0, 0.0, 0
+    for h in range(n_heads):
+        masses, supports = [], {}
+        for t, (q, k, v) in wl.head_steps(0, h):
+            Q, K, V = (oracle.bf16_to_f64(x) for x in (q, k, v))
+            if t < td:
+                masses.append(oracle.block_mass(Q, K, sc, B))
+                continue
+            if not supports:
+                mbar = oracle.mean_block_mass(masses)
+                supports = {qb: oracle.select_support(mbar[qb], qb, cfg.eta, cfg.cap)
+                            for qb in range(cfg.n_blocks)}
+            t0 = time.perf_counter()
+            oracle.masked_attention(Q, K, V, supports, B, sc)
+            t_late += time.perf_counter() - t0
+            n_late += 1
+            n_pairs = 0
+            for qb, sup in supports.items():
+                n_pairs += B * B * (len(sup) - 1) + B * (B + 1) // 2
+            flops += 4.0 * cfg.head_dim * n_pairs
+    return {"value": flops / t_late / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"heads 0..{n_heads - 1} of batch 0 of {cfg.name}: {td} dense discovery "
+                       f"steps + selection each, then {n_late} late masked-attention head-steps "
+                       f"timed ({t_late:.1f} s); algorithmic FLOPs of the sample's supports"),
+            "host_cpus": os.cpu_count()}
+
+
+def main(argv=None):
+    args = parse(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the WISE path here runs on a single MI355X "
+              "(per-(batch, head) sharding across GPUs is a design note, not built).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_wise_amd as wise
+    from wise_inputs import CONFIGS, Workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    wise.load_library()
+    cfg = CONFIGS[args.config]
+    T, td, B, D = cfg.steps, cfg.td, cfg.block, cfg.head_dim
+    dev = torch.device("cuda:0")
+
+    log(f"generating {T} steps of {cfg.name} inputs")
+    t0 = time.time()
+    qs, ks, vs = [], [], []
+    for t, q, k, v in Workload(cfg, threads=min(16, os.cpu_count() or 1)).steps():
+        for src, dst in ((q, qs), (k, ks), (v, vs)):
+            dst.append(torch.from_numpy(src.view(np.int16)).view(torch.bfloat16).to(dev))
+    log(f"inputs ready in {time.time() - t0:.1f} s")
+
+    nb = cfg.n_blocks
+    mass = torch.zeros(cfg.batch, cfg.heads, nb, nb, dtype=torch.float32, device=dev)
+    outs = [torch.empty_like(qs[0]) for _ in range(T)]
+    n_rows = cfg.batch * cfg.heads * nb
+    row_ptr = torch.empty(n_rows + 1, dtype=torch.int32, device=dev)
+    cap = wise.wise_select_max_nnz(cfg.batch, cfg.heads, cfg.seq_len, D, B, cfg.cap)
+    col_idx = torch.empty(cap, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def trajectory(record=False):
+        if record:
+            ev[0].record(stream)
+        mass.zero_()
+        for t in range(td):
+            wise.wise_full_attn_accum(qs[t], ks[t], vs[t], mass, B, o=outs[t])
+        if record:
+            ev[1].record(stream)
+        wise.wise_select_support(mass, td, cfg.eta, D, B, cfg.cap, row_ptr=row_ptr, col_idx=col_idx)
+        if record:
+            ev[2].record(stream)
+        for t in range(td, T):
+            wise.wise_sparse_attn(qs[t], ks[t], vs[t], row_ptr, col_idx, B, o=outs[t])
+        if record:
+            ev[3].record(stream)
+
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.calibrate_copy} MiB read + {args.calibrate_copy} MiB written, x3")
+        del src, dst
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        trajectory()
+    torch.cuda.synchronize()
+
+    per = {"k1": [], "k3": [], "k4": []}
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for _ in range(args.steps):
+        trajectory(record=True)
+        ev[3].synchronize()
+        per["k1"].append(ev[0].elapsed_time(ev[1]))
+        per["k3"].append(ev[1].elapsed_time(ev[2]))
+        per["k4"].append(ev[2].elapsed_time(ev[3]))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    log(f"timed {args.steps} trajectories in {wall:.3f} s")
+
+    rp_h = row_ptr.cpu().numpy()
+    fc = flop_counts(cfg, rp_h)
+
+    # Dense baseline on the same late-step inputs (the speedup denominator).
+    def dense_late():
+        for t in range(td, T):
+            wise.wise_full_attn(qs[t], ks[t], vs[t], B, o=outs[t])
+    for _ in range(args.warmup):
+        dense_late()
+    dts = []
+    for _ in range(args.steps):
+        ev[0].record(stream)
+        dense_late()
+        ev[1].record(stream)
+        ev[1].synchronize()
+        dts.append(ev[0].elapsed_time(ev[1]))
+
+    # Same backend on every causal block (full-support CSR), on request.
+    fts = []
+    full_rp = torch.from_numpy(np.concatenate([[0], np.cumsum(
+        np.tile(np.arange(1, nb + 1), cfg.batch * cfg.heads))]).astype(np.int32)).to(dev)
+    full_ci = torch.from_numpy(np.tile(np.concatenate([np.arange(q + 1) for q in range(nb)]),
+                                       cfg.batch * cfg.heads).astype(np.int32)).to(dev)
+
+    def full_sparse():
+        for t in range(td, T):
+            wise.wise_sparse_attn(qs[t], ks[t], vs[t], full_rp, full_ci, B, o=outs[t])
+    if args.same_backend:
+        for _ in range(args.warmup):
+            full_sparse()
+        for _ in range(max(3, args.steps // 4)):
+            ev[0].record(stream)
+            full_sparse()
+            ev[1].record(stream)
+            ev[1].synchronize()
+            fts.append(ev[0].elapsed_time(ev[1]))
+
+    med = lambda xs: float(np.median(xs))
+    n_late = T - td
+    k4_ms = med(per["k4"]) / n_late            # one sparse launch
+    k1_ms = med(per["k1"]) / td                # one discovery launch (incl. the mass memset share)
+    k3_ms = med(per["k3"])
+    k2_ms = med(dts) / n_late                  # one dense launch
+    kfull_ms = med(fts) / n_late if fts else None
+    value = fc["sparse_exec"] / (k4_ms * 1e-3) / 1e12
+    alg_tflops = fc["sparse_alg"] / (k4_ms * 1e-3) / 1e12
+    step_ms = wall / args.steps * 1e3
+    traffic = measured_traffic() if args.config == "ctx4k" else None
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": (f"{cfg.name}: recurrent attention trajectory, batch {cfg.batch}, "
+                                f"{cfg.heads} heads, head_dim {D}, seq {cfg.seq_len}, block {B}, "
+                                f"T {T}, td {td}, eta {cfg.eta}, cap {cfg.cap}"),
+                   "batch": cfg.batch, "heads": cfg.heads, "seq_len": cfg.seq_len,
+                   "head_dim": D, "block": B, "recurrent_steps": T, "td": td, "eta": cfg.eta,
+                   "parallelism": "single-gpu"},
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "late_step_speedup_vs_dense": round(k2_ms / k4_ms, 3),
+        "ideal_speedup_1_over_density": round(1.0 / fc["density_adm"], 3),
+        "setup_inclusive_speedup": round(n_late * k2_ms / (k3_ms + n_late * k4_ms), 3),
+        "trajectory_speedup": round(T * k2_ms / (td * k1_ms + k3_ms + n_late * k4_ms), 3),
+        "same_backend_full_vs_support": round(kfull_ms / k4_ms, 3) if kfull_ms else None,
+        "density_admissible": round(fc["density_adm"], 4),
+        "density_full_grid": round(fc["density_full"], 4),
+        "kernel_ms": {"sparse_attn": round(k4_ms, 4), "full_attn_accum": round(k1_ms, 4),
+                      "select_support": round(k3_ms, 4), "full_attn": round(k2_ms, 4),
+                      "sparse_attn_full_csr": round(kfull_ms, 4) if kfull_ms else None},
+        "dense_tflops_exec": round(fc["dense_exec"] / (k2_ms * 1e-3) / 1e12, 2),
+        "accum_tflops_exec": round(fc["dense_exec"] / (k1_ms * 1e-3) / 1e12, 2),
+        "sparse_tflops_algorithmic": round(alg_tflops, 2),
+        "roofline": {"bound": "mfma", "kernel": "wise_attn_kernel<128,64,64,sparse>",
+                     "achieved": round(alg_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(alg_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "traffic_unit": "bytes per launch (HBM read + write, rocprofv3 counters)",
+                     "traffic_GBps": round(traffic / (k4_ms * 1e-3) / 1e9, 1) if traffic else None,
+                     "compulsory_GBps": round(sparse_bytes(cfg, fc["nnz"], fc["n_rows"]) /
+                                              (k4_ms * 1e-3) / 1e9, 1)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a sample (cpu_baseline)")
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_heads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
