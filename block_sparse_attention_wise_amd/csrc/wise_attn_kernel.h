@@ -35,12 +35,12 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kTau = 8.0f;  // lazy-rescale slack, log2 units
 
-// (a.lo16, b.lo16) and (a.hi16, b.hi16) as packed 32-bit words.
+// (a.lo16, b.lo16) and (a.hi16, b.hi16) as packed 32-bit words (one v_perm_b32).
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-  return (a & 0xFFFFu) | (b << 16);
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
 }
 __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xFFFF0000u);
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
 template <int D, int BLK, int KT>
@@ -64,7 +64,8 @@ struct AttnShape {
 template <int D, int BLK, int KT>
 __host__ __device__ constexpr size_t attn_lds_need(int mode, int nblk) {
   return AttnShape<D, BLK, KT>::kTileLds +
-         (mode == kDenseMass ? ((size_t)nblk * (BLK + 1) + BLK) * 4 : 0);
+         (mode == kDenseMass ? ((size_t)nblk * (BLK + 1) + BLK) * 4 : 0) +
+         (mode == kSparse ? ((size_t)nblk + 1) * 4 : 0);
 }
 
 // Stored position of key kappa (0..KT-1) inside a V^T row: within each
@@ -77,22 +78,24 @@ __device__ __forceinline__ int vt_pos(int kappa) {
   return (kappa & ~15) | (sq << 2) | (kappa & 3);
 }
 
-// Global -> VGPR prefetch of one key tile: K as 16-byte row chunks, V as
-// 4-key x 8-dim pieces (so they can be transposed on the way into LDS).
+// Global -> VGPR prefetch of one key tile, through buffer resources that
+// span one head of K and V (hardware-checked bounds, scalar tile offset,
+// lane offsets fixed for the whole kernel).  K is a contiguous run of KT
+// rows, read as 16-byte chunks; V is read as 4-key x 8-dim pieces so they
+// can be transposed on the way into LDS.
 template <int D, int BLK, int KT>
-__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ Kh, const uint16_t* __restrict__ Vh,
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
                                           int key0, int tid,
                                           u32x4_t (&kreg)[AttnShape<D, BLK, KT>::kKPer],
                                           u32x4_t (&vreg)[AttnShape<D, BLK, KT>::kVPer][4]) {
   using Sh = AttnShape<D, BLK, KT>;
   constexpr int NT = Sh::kThreads;
+  const int tile_off = key0 * D * 2;
 #pragma unroll
   for (int i = 0; i < Sh::kKPer; ++i) {
     const int u = tid + i * NT;
-    if (Sh::kKUnits % NT == 0 || u < Sh::kKUnits) {
-      const int r = u / (D / 8), c8 = u % (D / 8);
-      kreg[i] = *reinterpret_cast<const u32x4_t*>(Kh + (size_t)(key0 + r) * D + c8 * 8);
-    }
+    if (Sh::kKUnits % NT == 0 || u < Sh::kKUnits)
+      kreg[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(krs, u * 16, tile_off, 0));
   }
 #pragma unroll
   for (int i = 0; i < Sh::kVPer; ++i) {
@@ -101,7 +104,8 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ Kh, const
       const int a = u % (KT / 4), dc = u / (KT / 4);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        vreg[i][j] = *reinterpret_cast<const u32x4_t*>(Vh + (size_t)(key0 + 4 * a + j) * D + dc * 8);
+        vreg[i][j] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, (4 * a + j) * D * 2 + dc * 16, tile_off, 0));
     }
   }
 }
@@ -148,16 +152,79 @@ __device__ __forceinline__ void store_tile(uint16_t* Ks, uint16_t* Vt, int tid,
   }
 }
 
+// Scores of one key tile -> P (bf16 operands) and running statistics.
+// MASKED applies the causal mask key > query (diagonal block only).
+template <int D, int BLK, int KT, int MODE, bool MASKED>
+__device__ __forceinline__ void softmax_tile(float* part, float scale_log2, int rel, int g, int n,
+                                             int wave, int kb, float& m_ref, float& l_part,
+                                             float& blk_part,
+                                             f32x16_t (&s)[AttnShape<D, BLK, KT>::kM],
+                                             bf16x8_t (&pf)[AttnShape<D, BLK, KT>::kM][2],
+                                             f32x16_t (&oacc)[AttnShape<D, BLK, KT>::kDTiles]) {
+  using Sh = AttnShape<D, BLK, KT>;
+  if constexpr (MASKED) {
+    // key offset within the tile > query offset within the tile -> -inf
+#pragma unroll
+    for (int m = 0; m < Sh::kM; ++m)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int koff = m * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+        s[m][i] = (koff > rel) ? -INFINITY : s[m][i];
+      }
+  }
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int m = 0; m < Sh::kM; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[m][i]);
+  const float tmax2 = tmax * scale_log2;  // scale > 0: max commutes with scaling
+
+  if (__any(tmax2 > m_ref + kTau)) {
+    // Rare path: raise the reference max of the queries that need it and
+    // rescale everything accumulated relative to the old one.
+    const float rmax = fmaxf(tmax2, __shfl_xor(tmax2, 32));
+    const float m_new = (rmax > m_ref + kTau) ? rmax : m_ref;
+    const float f = (m_new == m_ref) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+#pragma unroll
+    for (int t = 0; t < Sh::kDTiles; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[t][i] *= f;
+    l_part *= f;
+    if constexpr (MODE == kDenseMass) {
+      blk_part *= f;
+      if (g == 0 && f != 1.f)
+        for (int b = 0; b < kb; ++b) part[b * (BLK + 1) + wave * 32 + n] *= f;
+    }
+    m_ref = m_new;
+  }
+
+  // P = exp2(s * scale*log2e - m); masked scores are -inf and give 0.
+  const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
+  float tsum = 0.f;
+#pragma unroll
+  for (int m = 0; m < Sh::kM; ++m)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(s[m][kk * 8 + e], scale_log2, neg_m));
+        tsum += pv;
+        pf[m][kk][e] = (__bf16)pv;
+      }
+  l_part += tsum;
+  if constexpr (MODE == kDenseMass) blk_part += tsum;
+}
+
 template <int D, int BLK, int KT, int MODE>
 __global__ void __launch_bounds__(64 * (BLK / 32), 2) wise_attn_kernel(AttnParams p) {
   using Sh = AttnShape<D, BLK, KT>;
-  constexpr int NT = Sh::kThreads;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);
   uint16_t* Vt = Ks + KT * Sh::kKsStride;
-  float* part = reinterpret_cast<float*>(Vt + D * Sh::kVtStride);  // [nblk][BLK+1]
-  float* invl = part + (size_t)p.nblk * (BLK + 1);                  // [BLK]
+  int32_t* blist = reinterpret_cast<int32_t*>(Vt + D * Sh::kVtStride);   // kSparse: [nblk + 1]
+  float* part = reinterpret_cast<float*>(Vt + D * Sh::kVtStride);       // kDenseMass: [nblk][BLK+1]
+  float* invl = part + (size_t)p.nblk * (BLK + 1);                      // kDenseMass: [BLK]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -182,13 +249,49 @@ __global__ void __launch_bounds__(64 * (BLK / 32), 2) wise_attn_kernel(AttnParam
   for (int c = 0; c < Sh::kChunks; ++c)
     qf[c] = *reinterpret_cast<const bf16x8_t*>(Qh + (size_t)qrow * D + c * 16 + 8 * g);
 
-  int e_begin = 0, e_end = qb + 1;
-  if (MODE == kSparse) {
-    e_begin = p.row_ptr[row];
-    e_end = p.row_ptr[row + 1];
-    if (e_end < e_begin) e_end = e_begin;
+  // Key blocks of this row.  Dense: 0..qb.  Sparse: the CSR row, compacted
+  // into LDS by wave 0; entries out of [0, qb], repeated or not ascending
+  // are dropped, so every listed block is read once and the diagonal block,
+  // if listed, is last.
+  int n_blk = qb + 1;
+  bool has_diag = true;
+  if constexpr (MODE == kSparse) {
+    if (wave == 0) {
+      int e_begin = p.row_ptr[row];
+      int e_end = p.row_ptr[row + 1];
+      if (e_end < e_begin) e_end = e_begin;
+      int carry = -1, count = 0;
+      for (int base = e_begin; base < e_end; base += 64) {
+        const int idx = base + lane;
+        const int c = idx < e_end ? p.col_idx[idx] : -1;
+        const bool inr = idx < e_end && c >= 0 && c <= qb;
+        int incl = inr ? c : -1;  // inclusive prefix max over lanes
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(incl, off);
+          if (lane >= off) incl = max(incl, y);
+        }
+        int excl = __shfl_up(incl, 1);
+        if (lane == 0) excl = -1;
+        excl = max(excl, carry);
+        const bool acc = inr && c > excl;
+        const uint64_t bal = __ballot(acc);
+        if (acc) blist[1 + count + __popcll(bal & ((1ull << lane) - 1ull))] = c;
+        count += __popcll(bal);
+        carry = max(carry, __shfl(incl, 63));
+      }
+      if (lane == 0) blist[0] = count;
+    }
+    __syncthreads();
+    n_blk = __builtin_amdgcn_readfirstlane(blist[0]);
+    has_diag = n_blk > 0 && __builtin_amdgcn_readfirstlane(blist[n_blk]) == qb;
   }
-  const int n_tiles = (e_end - e_begin) * Sh::kSub;
+  auto block_of = [&](int e) -> int {
+    if constexpr (MODE == kSparse) return __builtin_amdgcn_readfirstlane(blist[1 + e]);
+    else return e;
+  };
+  const int n_tiles = n_blk * Sh::kSub;
+  const int n_main = (n_blk - (has_diag ? 1 : 0)) * Sh::kSub;  // tiles without masking
 
   f32x16_t oacc[Sh::kDTiles];
 #pragma unroll
@@ -202,49 +305,30 @@ __global__ void __launch_bounds__(64 * (BLK / 32), 2) wise_attn_kernel(AttnParam
   u32x4_t kreg[Sh::kKPer];
   u32x4_t vreg[Sh::kVPer][4];
 
-  // Tile bookkeeping (wave-uniform).  A sparse entry that is out of range,
-  // not ascending or a duplicate is ignored: its tile is loaded from block 0
-  // (always in bounds) and fully masked.
-  int ld_prev = -1;   // last accepted block id on the load side
-  int ld_kb = 0, ld_ok = 1;
+  // Buffer resources over this head's K and V (word 3: raw 32-bit data format).
+  const int head_bytes = p.seq * D * 2;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Kh), 0, head_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Vh), 0, head_bytes, 0x00020000);
 
-  auto entry_block = [&](int it, int& kb, int& ok) {
+  if (n_tiles > 0) load_tile<D, BLK, KT>(krs, vrs, block_of(0) * BLK, tid, kreg, vreg);
+
+  // One pipeline step: publish the prefetched tile, prefetch the next one,
+  // then compute on the published tile.
+  auto step = [&]<bool MASKED>(int it) __attribute__((always_inline)) {
     const int sub = it % Sh::kSub;
-    if (MODE == kSparse) {
-      if (sub == 0) {
-        int c = p.col_idx[e_begin + it / Sh::kSub];
-        ld_ok = (c >= 0 && c <= qb && c > ld_prev) ? 1 : 0;
-        ld_kb = ld_ok ? c : 0;
-        if (ld_ok) ld_prev = c;
-      }
-      kb = ld_kb;
-      ok = ld_ok;
-    } else {
-      kb = e_begin + it / Sh::kSub;
-      ok = 1;
-    }
-  };
-
-  int kb_cur = 0, ok_cur = 1;
-  if (n_tiles > 0) {
-    entry_block(0, kb_cur, ok_cur);
-    load_tile<D, BLK, KT>(Kh, Vh, kb_cur * BLK, tid, kreg, vreg);
-  }
-
-  for (int it = 0; it < n_tiles; ++it) {
-    const int sub = it % Sh::kSub;
-    const int kb = kb_cur, ok = ok_cur;
+    const int kb = block_of(it / Sh::kSub);
     const int key0 = kb * BLK + sub * KT;
 
     __syncthreads();  // previous tile fully consumed
     store_tile<D, BLK, KT>(Ks, Vt, tid, kreg, vreg);
     __syncthreads();
-    if (it + 1 < n_tiles) {
-      entry_block(it + 1, kb_cur, ok_cur);
-      load_tile<D, BLK, KT>(Kh, Vh, kb_cur * BLK + ((it + 1) % Sh::kSub) * KT, tid, kreg, vreg);
-    }
+    if (it + 1 < n_tiles)
+      load_tile<D, BLK, KT>(krs, vrs, block_of((it + 1) / Sh::kSub) * BLK + ((it + 1) % Sh::kSub) * KT,
+                            tid, kreg, vreg);
 
-    // ---- S^T = K Q^T ----------------------------------------------------
+    // S^T = K Q^T
     f32x16_t s[Sh::kM];
 #pragma unroll
     for (int m = 0; m < Sh::kM; ++m) {
@@ -258,59 +342,11 @@ __global__ void __launch_bounds__(64 * (BLK / 32), 2) wise_attn_kernel(AttnParam
       }
     }
 
-    // ---- scores in log2 units, causal mask on the diagonal block ---------
-    const bool diag = (kb == qb) || !ok;
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int m = 0; m < Sh::kM; ++m)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = s[m][i] * p.scale_log2;
-        if (diag) {
-          const int key = key0 + m * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (!ok || key > qrow) x = -INFINITY;
-        }
-        s[m][i] = x;
-        tmax = fmaxf(tmax, x);
-      }
-
-    if (__any(tmax > m_ref + kTau)) {
-      // Rare path: raise the reference max of the queries that need it and
-      // rescale everything accumulated relative to the old one.
-      const float rmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = (rmax > m_ref + kTau) ? rmax : m_ref;
-      const float f = (m_new == m_ref) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-#pragma unroll
-      for (int t = 0; t < Sh::kDTiles; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[t][i] *= f;
-      l_part *= f;
-      if (MODE == kDenseMass) {
-        blk_part *= f;
-        if (g == 0 && f != 1.f)
-          for (int b = 0; b < kb; ++b) part[b * (BLK + 1) + wave * 32 + n] *= f;
-      }
-      m_ref = m_new;
-    }
-
-    // ---- P = exp2(x - m), row sums, bf16 operands -------------------------
-    const float mr = (m_ref == -INFINITY) ? 0.f : m_ref;
     bf16x8_t pf[Sh::kM][2];
-    float tsum = 0.f;
-#pragma unroll
-    for (int m = 0; m < Sh::kM; ++m)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pv = __builtin_amdgcn_exp2f(s[m][kk * 8 + e] - mr);
-          tsum += pv;
-          pf[m][kk][e] = (__bf16)pv;
-        }
-    l_part += tsum;
-    if (MODE == kDenseMass) blk_part += tsum;
+    softmax_tile<D, BLK, KT, MODE, MASKED>(part, p.scale_log2, qrow - key0, g, n, wave, kb, m_ref,
+                                           l_part, blk_part, s, pf, oacc);
 
-    // ---- O^T += V^T P^T ---------------------------------------------------
+    // O^T += V^T P^T
 #pragma unroll
     for (int t = 0; t < Sh::kDTiles; ++t)
 #pragma unroll
@@ -322,12 +358,18 @@ __global__ void __launch_bounds__(64 * (BLK / 32), 2) wise_attn_kernel(AttnParam
           oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[m][kk], oacc[t], 0, 0, 0);
         }
 
-    if (MODE == kDenseMass && sub == Sh::kSub - 1) {
-      const float bp = blk_part + __shfl_xor(blk_part, 32);
-      if (g == 0) part[kb * (BLK + 1) + wave * 32 + n] = bp;
-      blk_part = 0.f;
+    if constexpr (MODE == kDenseMass) {
+      if (sub == Sh::kSub - 1) {
+        const float bp = blk_part + __shfl_xor(blk_part, 32);
+        if (g == 0) part[kb * (BLK + 1) + wave * 32 + n] = bp;
+        blk_part = 0.f;
+      }
     }
-  }
+  };
+
+  int it = 0;
+  for (; it < n_main; ++it) step.template operator()<false>(it);
+  for (; it < n_tiles; ++it) step.template operator()<true>(it);
 
   // ---- epilogue -----------------------------------------------------------
   const float lt = l_part + __shfl_xor(l_part, 32);
@@ -352,11 +394,11 @@ __global__ void __launch_bounds__(64 * (BLK / 32), 2) wise_attn_kernel(AttnParam
     p.lse[(size_t)bh * p.seq + qrow] = lse;
   }
 
-  if (MODE == kDenseMass) {
+  if constexpr (MODE == kDenseMass) {
     if (g == 0) invl[wave * 32 + n] = inv;
     __syncthreads();
     float* mrow = p.mass + (size_t)row * p.nblk;
-    for (int b = tid; b <= qb; b += NT) {
+    for (int b = tid; b <= qb; b += Sh::kThreads) {
       const float* pr = part + b * (BLK + 1);
       float acc = 0.f;
       for (int i = 0; i < BLK; ++i) acc = fmaf(pr[i], invl[i], acc);
@@ -388,6 +430,11 @@ template <int D, int BLK>
 int choose_kt(int mode, int nblk) {
   if constexpr (BLK == 32) {
     return attn_lds_need<D, 32, 32>(mode, nblk) <= kMaxLds ? 32 : 0;
+  } else if constexpr (BLK == 64 && D == 128) {
+    // The mass mode's extra live state does not fit 64-key tiles in 256 VGPRs.
+    if (mode != kDenseMass && attn_lds_need<D, BLK, 64>(mode, nblk) <= kMaxLds) return 64;
+    if (attn_lds_need<D, BLK, 32>(mode, nblk) <= kMaxLds) return 32;
+    return 0;
   } else {
     if (attn_lds_need<D, BLK, 64>(mode, nblk) <= kMaxLds) return 64;
     if (attn_lds_need<D, BLK, 32>(mode, nblk) <= kMaxLds) return 32;
