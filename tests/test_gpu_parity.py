@@ -9,8 +9,9 @@ import pytest
 
 import oracle
 from wise_inputs import CONFIGS, Workload
-from wise_testlib import (MAX_ABS, MEAN_ABS, bf16_dev_to_f64, compare_outputs, csr_rows,
-                          mass_tolerance, say, support_ok, to_dev)
+from wise_testlib import (MAX_ABS, MEAN_ABS, bf16_dev_to_f64, check_trajectory_rows,
+                          compare_outputs, csr_rows, mass_tolerance, run_trajectory, say,
+                          support_ok, to_dev)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -303,82 +304,13 @@ def test_deterministic_repeat():
     assert torch.equal(c1[:n], c2[:n]) and torch.equal(s1, s2)
 
 
-def _run_trajectory(cfg, steps):
-    nb = cfg.n_blocks
-    mass = torch.zeros(cfg.batch, cfg.heads, nb, nb, dtype=torch.float32, device="cuda")
-    outs = []
-    row_ptr = col_idx = None
-    for t, q, k, v in steps:
-        qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
-        if t < cfg.td:
-            outs.append(wise.wise_full_attn_accum(qd, kd, vd, mass, cfg.block))
-        else:
-            if row_ptr is None:
-                row_ptr, col_idx = wise.wise_select_support(mass, cfg.td, cfg.eta, cfg.head_dim,
-                                                            cfg.block, cfg.cap)
-            outs.append(wise.wise_sparse_attn(qd, kd, vd, row_ptr, col_idx, cfg.block))
-    torch.cuda.synchronize()
-    return mass, row_ptr, col_idx, outs
-
-
-def check_trajectory_rows(cfg, gpu_mass, gpu_rows, gpu_outs, samples, head_steps_fn,
-                          out_steps=None):
-    """Compare sampled (b, h, q) rows of a GPU trajectory with the oracle.
-
-    Masses within tolerance; supports equal wherever the oracle's Appendix A.1
-    margin Delta_q exceeds the measured mass error of that row (then no
-    perturbation of that size can change the support), otherwise the GPU
-    support must be the oracle's selection on the GPU's own masses; outputs
-    within tolerance, recomputed with the GPU's support where it differs.
-    """
-    nb, td, B = cfg.n_blocks, cfg.td, cfg.block
-    sc = oracle.default_scale(cfg.head_dim)
-    by_head = {}
-    for (b, h, qb) in samples:
-        by_head.setdefault((b, h), []).append(qb)
-    stats = {"rows": 0, "margin_rows": 0, "max_abs": 0.0, "mean_abs": []}
-    for (b, h), qbs in by_head.items():
-        steps = [(q, k, v) for _, (q, k, v) in head_steps_fn(b, h)]
-        steps64 = [tuple(oracle.bf16_to_f64(x) for x in s) for s in steps]
-        ref = oracle.trajectory_head(steps64, td, B, cfg.eta, cfg.cap, qblocks=qbs, out_rows=False)
-        for i, qb in enumerate(qbs):
-            r = (b * cfg.heads + h) * nb + qb
-            gm = gpu_mass[b, h, qb].astype(np.float64)
-            err = np.abs(gm - ref["mass_sum"][i])
-            assert err.max() <= mass_tolerance(td), (b, h, qb, err.max())
-            mbar_gpu = gm / td
-            mbar_ref = ref["mass_mean"][i]
-            sup_gpu = gpu_rows[r]
-            sup_ref = ref["supports"][qb]
-            row_err = float(np.abs(mbar_gpu - mbar_ref)[:qb + 1].max())
-            delta = ref["margins"][qb]["Delta"]
-            if sup_gpu != sup_ref:
-                assert delta <= row_err + 1e-12, (b, h, qb, sup_gpu, sup_ref, delta, row_err)
-                ok, _ = support_ok(sup_gpu, mbar_gpu, qb, cfg.eta, cfg.cap)
-                assert ok, (b, h, qb, sup_gpu)
-                stats["margin_rows"] += 1
-            stats["rows"] += 1
-            rows = np.arange(qb * B, (qb + 1) * B)
-            for t in (range(cfg.steps) if out_steps is None else out_steps):
-                Q, K, V = steps64[t]
-                if t < td:
-                    want = oracle.dense_attention(Q, K, V, sc, rows)
-                else:
-                    want = oracle.masked_attention(Q, K, V, {qb: sup_gpu}, B, sc, rows)
-                got = gpu_outs(t, b, h, rows)
-                mx, mn = compare_outputs(got, want, f"O t{t} b{b}h{h}q{qb}")
-                stats["max_abs"] = max(stats["max_abs"], mx)
-                stats["mean_abs"].append(mn)
-    return stats
-
-
 def test_tiny_trajectory_end_to_end():
     """The tiny workload (4 heads, d 64, seq 256, B 32, T 4, td 2, eta 0.9)
     through all four calls, every row checked."""
     cfg = CONFIGS["tiny"]
     say("tiny trajectory")
     steps = _steps(cfg)
-    mass, row_ptr, col_idx, outs = _run_trajectory(cfg, steps)
+    mass, row_ptr, col_idx, outs = run_trajectory(cfg, steps)
     gm = mass.cpu().numpy()
     rows = csr_rows(row_ptr.cpu().numpy(), col_idx.cpu().numpy())
     outs_h = [bf16_dev_to_f64(o) for o in outs]
@@ -400,7 +332,7 @@ def test_small_trajectories_end_to_end():
                 CONFIGS["long"].with_(heads=2, seq_len=2048, steps=4, td=2, cap=6)):
         say(f"trajectory {cfg.name} {cfg.batch}x{cfg.heads} S{cfg.seq_len}")
         steps = _steps(cfg)
-        mass, row_ptr, col_idx, outs = _run_trajectory(cfg, steps)
+        mass, row_ptr, col_idx, outs = run_trajectory(cfg, steps)
         gm = mass.cpu().numpy()
         rows = csr_rows(row_ptr.cpu().numpy(), col_idx.cpu().numpy())
         outs_h = [bf16_dev_to_f64(o) for o in outs]
