@@ -47,18 +47,22 @@ template <int D, int BLK, int KT>
 struct AttnShape {
   static constexpr int kWaves = BLK / 32;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kKsStride = D + 8;    // u16 per K row in LDS (16 B pad)
-  static constexpr int kVtStride = KT + 8;   // u16 per V^T row in LDS (16 B pad)
+  // LDS row strides (u16 elements).  K rows: D/8 + 1 chunks of 16 bytes (odd,
+  // so the 16 rows read per pass by the QK operand land on distinct banks).
+  // V rows: (stride in chunks) % 16 in {4, 12}, so the transposing reads of
+  // 4 rows x 4 chunks per pass and the 16-chunk row stores are conflict free.
+  static constexpr int kKsStride = D + 8;
+  static constexpr int kVChunks = (D / 8) % 16 == 4 || (D / 8) % 16 == 12 ? D / 8 : D / 8 + 4;
+  static constexpr int kVStride = kVChunks * 8;
   static constexpr int kSub = BLK / KT;      // key tiles per key block
   static constexpr int kChunks = D / 16;     // K-steps of the QK^T product
   static constexpr int kDTiles = D / 32;     // 32-wide output column tiles
   static constexpr int kM = KT / 32;         // 32-key sub-tiles per key tile
-  static constexpr int kKUnits = KT * D / 8;         // 16-byte chunks of a K tile
-  static constexpr int kVUnits = (KT / 4) * (D / 8); // 4-key x 8-dim pieces of V
-  static constexpr int kKPer = (kKUnits + kThreads - 1) / kThreads;
-  static constexpr int kVPer = (kVUnits + kThreads - 1) / kThreads;
-  static constexpr size_t kTileLds = (size_t)KT * kKsStride * 2 + (size_t)D * kVtStride * 2;
+  static constexpr int kUnits = KT * D / 8;  // 16-byte chunks of a K or V tile
+  static constexpr int kPer = (kUnits + kThreads - 1) / kThreads;
+  static constexpr size_t kTileLds = (size_t)KT * kKsStride * 2 + (size_t)KT * kVStride * 2;
   static_assert(D % 32 == 0 && BLK % KT == 0 && KT % 32 == 0, "tile shape");
+  static_assert(kVChunks % 16 == 4 || kVChunks % 16 == 12, "V stride");
 };
 
 template <int D, int BLK, int KT>
@@ -68,98 +72,53 @@ __host__ __device__ constexpr size_t attn_lds_need(int mode, int nblk) {
          (mode == kSparse ? ((size_t)nblk + 1) * 4 : 0);
 }
 
-// Stored position of key kappa (0..KT-1) inside a V^T row: within each
-// group of 16 keys the key quads are stored in the order 0, 2, 1, 3, so the
-// 8 keys an MFMA lane group needs ({4g..4g+3} and {8+4g..8+4g+3}) are
-// contiguous.
-__device__ __forceinline__ int vt_pos(int kappa) {
-  int quad = (kappa >> 2) & 3;
-  int sq = (quad == 1) ? 2 : (quad == 2 ? 1 : quad);
-  return (kappa & ~15) | (sq << 2) | (kappa & 3);
-}
-
 // Global -> VGPR prefetch of one key tile, through buffer resources that
 // span one head of K and V (hardware-checked bounds, scalar tile offset,
-// lane offsets fixed for the whole kernel).  K is a contiguous run of KT
-// rows, read as 16-byte chunks; V is read as 4-key x 8-dim pieces so they
-// can be transposed on the way into LDS.
+// lane offsets fixed for the whole kernel).  A tile is a contiguous run of
+// KT rows of K (and of V), read as 16-byte chunks.
 template <int D, int BLK, int KT>
 __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
                                           int key0, int tid,
-                                          u32x4_t (&kreg)[AttnShape<D, BLK, KT>::kKPer],
-                                          u32x4_t (&vreg)[AttnShape<D, BLK, KT>::kVPer][4]) {
+                                          u32x4_t (&kreg)[AttnShape<D, BLK, KT>::kPer],
+                                          u32x4_t (&vreg)[AttnShape<D, BLK, KT>::kPer]) {
   using Sh = AttnShape<D, BLK, KT>;
   constexpr int NT = Sh::kThreads;
   const int tile_off = key0 * D * 2;
 #pragma unroll
-  for (int i = 0; i < Sh::kKPer; ++i) {
+  for (int i = 0; i < Sh::kPer; ++i) {
     const int u = tid + i * NT;
-    if (Sh::kKUnits % NT == 0 || u < Sh::kKUnits)
+    if (Sh::kUnits % NT == 0 || u < Sh::kUnits) {
       kreg[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(krs, u * 16, tile_off, 0));
-  }
-#pragma unroll
-  for (int i = 0; i < Sh::kVPer; ++i) {
-    const int u = tid + i * NT;
-    if (Sh::kVUnits % NT == 0 || u < Sh::kVUnits) {
-      const int a = u % (KT / 4), dc = u / (KT / 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        vreg[i][j] = __builtin_bit_cast(
-            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, (4 * a + j) * D * 2 + dc * 16, tile_off, 0));
+      vreg[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, u * 16, tile_off, 0));
     }
   }
 }
 
-// VGPR -> LDS: K row-major (padded rows), V transposed to [dim][key] with
-// the key order of vt_pos.
+// VGPR -> LDS: K and V both row-major with padded rows.
 template <int D, int BLK, int KT>
-__device__ __forceinline__ void store_tile(uint16_t* Ks, uint16_t* Vt, int tid,
-                                           const u32x4_t (&kreg)[AttnShape<D, BLK, KT>::kKPer],
-                                           const u32x4_t (&vreg)[AttnShape<D, BLK, KT>::kVPer][4]) {
+__device__ __forceinline__ void store_tile(uint16_t* Ks, uint16_t* Vs, int tid,
+                                           const u32x4_t (&kreg)[AttnShape<D, BLK, KT>::kPer],
+                                           const u32x4_t (&vreg)[AttnShape<D, BLK, KT>::kPer]) {
   using Sh = AttnShape<D, BLK, KT>;
   constexpr int NT = Sh::kThreads;
 #pragma unroll
-  for (int i = 0; i < Sh::kKPer; ++i) {
+  for (int i = 0; i < Sh::kPer; ++i) {
     const int u = tid + i * NT;
-    if (Sh::kKUnits % NT == 0 || u < Sh::kKUnits) {
+    if (Sh::kUnits % NT == 0 || u < Sh::kUnits) {
       const int r = u / (D / 8), c8 = u % (D / 8);
       *reinterpret_cast<u32x4_t*>(Ks + r * Sh::kKsStride + c8 * 8) = kreg[i];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < Sh::kVPer; ++i) {
-    const int u = tid + i * NT;
-    if (Sh::kVUnits % NT == 0 || u < Sh::kVUnits) {
-      const int a = u % (KT / 4), dc = u / (KT / 4);
-      uint16_t* dst = Vt + (dc * 8) * Sh::kVtStride + vt_pos(4 * a);
-      const u32x4_t k0 = vreg[i][0], k1 = vreg[i][1], k2 = vreg[i][2], k3 = vreg[i][3];
-      const uint32_t w0[4] = {k0.x, k0.y, k0.z, k0.w};
-      const uint32_t w1[4] = {k1.x, k1.y, k1.z, k1.w};
-      const uint32_t w2[4] = {k2.x, k2.y, k2.z, k2.w};
-      const uint32_t w3[4] = {k3.x, k3.y, k3.z, k3.w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        // dims 2h and 2h+1 of the 4 keys
-        u32x2_t even, odd;
-        even.x = pack_lo(w0[h], w1[h]);
-        even.y = pack_lo(w2[h], w3[h]);
-        odd.x = pack_hi(w0[h], w1[h]);
-        odd.y = pack_hi(w2[h], w3[h]);
-        *reinterpret_cast<u32x2_t*>(dst + (2 * h) * Sh::kVtStride) = even;
-        *reinterpret_cast<u32x2_t*>(dst + (2 * h + 1) * Sh::kVtStride) = odd;
-      }
+      *reinterpret_cast<u32x4_t*>(Vs + r * Sh::kVStride + c8 * 8) = vreg[i];
     }
   }
 }
 
-// Scores of one key tile -> P (bf16 operands) and running statistics.
-// MASKED applies the causal mask key > query (diagonal block only).
+// Scores of one key tile: causal mask (MASKED: diagonal block only), the
+// lazy-rescale check, and the rare rescale of everything accumulated so far.
 template <int D, int BLK, int KT, int MODE, bool MASKED>
-__device__ __forceinline__ void softmax_tile(float* part, float scale_log2, int rel, int g, int n,
+__device__ __forceinline__ void softmax_prep(float* part, float scale_log2, int rel, int g, int n,
                                              int wave, int kb, float& m_ref, float& l_part,
                                              float& blk_part,
                                              f32x16_t (&s)[AttnShape<D, BLK, KT>::kM],
-                                             bf16x8_t (&pf)[AttnShape<D, BLK, KT>::kM][2],
                                              f32x16_t (&oacc)[AttnShape<D, BLK, KT>::kDTiles]) {
   using Sh = AttnShape<D, BLK, KT>;
   if constexpr (MASKED) {
@@ -197,23 +156,10 @@ __device__ __forceinline__ void softmax_tile(float* part, float scale_log2, int 
     }
     m_ref = m_new;
   }
-
-  // P = exp2(s * scale*log2e - m); masked scores are -inf and give 0.
-  const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
-  float tsum = 0.f;
-#pragma unroll
-  for (int m = 0; m < Sh::kM; ++m)
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(s[m][kk * 8 + e], scale_log2, neg_m));
-        tsum += pv;
-        pf[m][kk][e] = (__bf16)pv;
-      }
-  l_part += tsum;
-  if constexpr (MODE == kDenseMass) blk_part += tsum;
 }
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 template <int D, int BLK, int KT, int MODE>
 __global__ void __launch_bounds__(64 * (BLK / 32), 2) wise_attn_kernel(AttnParams p) {
@@ -221,9 +167,9 @@ __global__ void __launch_bounds__(64 * (BLK / 32), 2) wise_attn_kernel(AttnParam
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* Vt = Ks + KT * Sh::kKsStride;
-  int32_t* blist = reinterpret_cast<int32_t*>(Vt + D * Sh::kVtStride);   // kSparse: [nblk + 1]
-  float* part = reinterpret_cast<float*>(Vt + D * Sh::kVtStride);       // kDenseMass: [nblk][BLK+1]
+  uint16_t* Vs = Ks + KT * Sh::kKsStride;
+  int32_t* blist = reinterpret_cast<int32_t*>(Vs + KT * Sh::kVStride);   // kSparse: [nblk + 1]
+  float* part = reinterpret_cast<float*>(Vs + KT * Sh::kVStride);       // kDenseMass: [nblk][BLK+1]
   float* invl = part + (size_t)p.nblk * (BLK + 1);                      // kDenseMass: [BLK]
 
   const int tid = threadIdx.x;
@@ -302,8 +248,15 @@ __global__ void __launch_bounds__(64 * (BLK / 32), 2) wise_attn_kernel(AttnParam
   float l_part = 0.f;       // this lane's share of the row sum
   float blk_part = 0.f;     // this lane's share of the current key block's mass
 
-  u32x4_t kreg[Sh::kKPer];
-  u32x4_t vreg[Sh::kVPer][4];
+  u32x4_t kreg[Sh::kPer];
+  u32x4_t vreg[Sh::kPer];
+
+  // Lane address of the PV operand (V^T, 32 dims x 16 keys) read with
+  // ds_read_b64_tr_b16: within each 16-lane group G = lane/16, source lane
+  // s = lane%16 points at row 4g + s/4 (+ 32m + 16kk + 8j) and dims
+  // 16(G%2) + 4(s%4) (+ 32dt); lane i of the group then receives 4
+  // consecutive keys at dim 16(G%2) + i, which is the A-operand layout.
+  const int v_lane_off = (4 * g + ((lane & 15) >> 2)) * Sh::kVStride + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   // Buffer resources over this head's K and V (word 3: raw 32-bit data format).
   const int head_bytes = p.seq * D * 2;
@@ -322,7 +275,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32), 2) wise_attn_kernel(AttnParam
     const int key0 = kb * BLK + sub * KT;
 
     __syncthreads();  // previous tile fully consumed
-    store_tile<D, BLK, KT>(Ks, Vt, tid, kreg, vreg);
+    store_tile<D, BLK, KT>(Ks, Vs, tid, kreg, vreg);
     __syncthreads();
     if (it + 1 < n_tiles)
       load_tile<D, BLK, KT>(krs, vrs, block_of((it + 1) / Sh::kSub) * BLK + ((it + 1) % Sh::kSub) * KT,
@@ -342,21 +295,53 @@ __global__ void __launch_bounds__(64 * (BLK / 32), 2) wise_attn_kernel(AttnParam
       }
     }
 
-    bf16x8_t pf[Sh::kM][2];
-    softmax_tile<D, BLK, KT, MODE, MASKED>(part, p.scale_log2, qrow - key0, g, n, wave, kb, m_ref,
-                                           l_part, blk_part, s, pf, oacc);
+    softmax_prep<D, BLK, KT, MODE, MASKED>(part, p.scale_log2, qrow - key0, g, n, wave, kb, m_ref,
+                                           l_part, blk_part, s, oacc);
 
-    // O^T += V^T P^T
+    // P = exp2(s * scale*log2e - m) per 32-key sub-tile, then that
+    // sub-tile's O^T += V^T P^T; the exponentials of sub-tile m+1 are
+    // independent of the MFMAs of sub-tile m.  Masked scores are -inf -> 0.
+    const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
+    float tsum = 0.f;
 #pragma unroll
-    for (int t = 0; t < Sh::kDTiles; ++t)
+    for (int m = 0; m < Sh::kM; ++m) {
+      bf16x8_t pf[2];
 #pragma unroll
-      for (int m = 0; m < Sh::kM; ++m)
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[m][kk * 8 + e], p.scale_log2, neg_m));
+          if constexpr (MODE == kDenseMass) tsum += pv;   // block mass needs the fp32 values
+          pf[kk][e] = (__bf16)pv;
+        }
+      if constexpr (MODE != kDenseMass) {
+        // Row sum of the bf16 operands themselves (the same values the PV
+        // product uses), two per packed dot product.
+        const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const bf16x2_t pair = {pf[kk][2 * w], pf[kk][2 * w + 1]};
+            tsum = __builtin_amdgcn_fdot2_f32_bf16(pair, one, tsum, false);
+          }
+      }
+#pragma unroll
+      for (int t = 0; t < Sh::kDTiles; ++t)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-              Vt + (t * 32 + n) * Sh::kVtStride + (2 * m + kk) * 16 + 8 * g);
-          oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[m][kk], oacc[t], 0, 0, 0);
+          const uint16_t* vp = Vs + v_lane_off + (32 * m + 16 * kk) * Sh::kVStride + 32 * t;
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(vp));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(vp + 8 * Sh::kVStride));
+          const bf16x8_t a =
+              __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], oacc[t], 0, 0, 0);
         }
+    }
+    l_part += tsum;
+    if constexpr (MODE == kDenseMass) blk_part += tsum;
 
     if constexpr (MODE == kDenseMass) {
       if (sub == Sh::kSub - 1) {

@@ -74,7 +74,9 @@ def test_dense_matches_oracle(shape):
             s[np.triu_indices(s_, 1)] = -np.inf
             m = s.max(axis=1)
             ref_lse = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
-            assert np.max(np.abs(lse_h[b, h] - ref_lse)) < 1e-3
+            # The row sum adds the bf16-rounded probabilities that the PV product
+            # uses (relative error <= 2^-9 each), so log(l) may move by ~2^-8.
+            assert np.max(np.abs(lse_h[b, h] - ref_lse)) < 4e-3
 
 
 @pytest.mark.parametrize("d_,blk", [(64, 32), (128, 64), (96, 128)])
