@@ -24,6 +24,9 @@
 // normalised by the query's final row sum in the epilogue.
 #pragma once
 
+#include <algorithm>
+#include <type_traits>
+
 #include "wise_internal.h"
 
 namespace wise {
@@ -43,9 +46,9 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
-template <int D, int BLK, int KT>
+template <int D, int BLK, int KT, int RPW = 1>
 struct AttnShape {
-  static constexpr int kWaves = BLK / 32;
+  static constexpr int kWaves = BLK / 32 * RPW;   // RPW rows of BLK queries per workgroup
   static constexpr int kThreads = 64 * kWaves;
   // LDS row strides (u16 elements).  K rows: D/8 + 1 chunks of 16 bytes (odd,
   // so the 16 rows read per pass by the QK operand land on distinct banks).
@@ -65,49 +68,43 @@ struct AttnShape {
   static_assert(kVChunks % 16 == 4 || kVChunks % 16 == 12, "V stride");
 };
 
-template <int D, int BLK, int KT>
+// Rows (query blocks) per workgroup: two adjacent rows for block 64, so
+// that four waves share every staged K/V tile (the two rows' key-block
+// lists overlap heavily), one row otherwise.  The mass mode keeps one row
+// when the per-(query, key block) partials of two rows would not fit.
+template <int D, int BLK, int KT, int RPW>
 __host__ __device__ constexpr size_t attn_lds_need(int mode, int nblk) {
-  return AttnShape<D, BLK, KT>::kTileLds +
-         (mode == kDenseMass ? ((size_t)nblk * (BLK + 1) + BLK) * 4 : 0) +
-         (mode == kSparse ? ((size_t)nblk + 1) * 4 : 0);
+  return AttnShape<D, BLK, KT, RPW>::kTileLds +
+         (mode == kDenseMass ? (size_t)RPW * ((size_t)nblk * (BLK + 1) + BLK) * 4 : 0) +
+         (mode == kSparse ? (size_t)RPW * ((nblk + 31) / 32) * 4 + ((size_t)nblk + 1) * 4 : 0);
 }
 
-// Global -> VGPR prefetch of one key tile, through buffer resources that
-// span one head of K and V (hardware-checked bounds, scalar tile offset,
-// lane offsets fixed for the whole kernel).  A tile is a contiguous run of
-// KT rows of K (and of V), read as 16-byte chunks.
-template <int D, int BLK, int KT>
-__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
-                                          int key0, int tid,
-                                          u32x4_t (&kreg)[AttnShape<D, BLK, KT>::kPer],
-                                          u32x4_t (&vreg)[AttnShape<D, BLK, KT>::kPer]) {
-  using Sh = AttnShape<D, BLK, KT>;
+template <int D, int BLK, int KT, int RPW>
+__device__ __forceinline__ void load_rows(__amdgpu_buffer_rsrc_t rs, int key0, int tid,
+                                          u32x4_t (&reg)[AttnShape<D, BLK, KT, RPW>::kPer]) {
+  using Sh = AttnShape<D, BLK, KT, RPW>;
   constexpr int NT = Sh::kThreads;
   const int tile_off = key0 * D * 2;
 #pragma unroll
   for (int i = 0; i < Sh::kPer; ++i) {
     const int u = tid + i * NT;
-    if (Sh::kUnits % NT == 0 || u < Sh::kUnits) {
-      kreg[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(krs, u * 16, tile_off, 0));
-      vreg[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, u * 16, tile_off, 0));
-    }
+    if (Sh::kUnits % NT == 0 || u < Sh::kUnits)
+      reg[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, u * 16, tile_off, 0));
   }
 }
 
-// VGPR -> LDS: K and V both row-major with padded rows.
-template <int D, int BLK, int KT>
-__device__ __forceinline__ void store_tile(uint16_t* Ks, uint16_t* Vs, int tid,
-                                           const u32x4_t (&kreg)[AttnShape<D, BLK, KT>::kPer],
-                                           const u32x4_t (&vreg)[AttnShape<D, BLK, KT>::kPer]) {
-  using Sh = AttnShape<D, BLK, KT>;
+// VGPR -> LDS, row-major with padded rows of STRIDE u16.
+template <int D, int BLK, int KT, int RPW, int STRIDE>
+__device__ __forceinline__ void store_rows(uint16_t* dst, int tid,
+                                           const u32x4_t (&reg)[AttnShape<D, BLK, KT, RPW>::kPer]) {
+  using Sh = AttnShape<D, BLK, KT, RPW>;
   constexpr int NT = Sh::kThreads;
 #pragma unroll
   for (int i = 0; i < Sh::kPer; ++i) {
     const int u = tid + i * NT;
     if (Sh::kUnits % NT == 0 || u < Sh::kUnits) {
       const int r = u / (D / 8), c8 = u % (D / 8);
-      *reinterpret_cast<u32x4_t*>(Ks + r * Sh::kKsStride + c8 * 8) = kreg[i];
-      *reinterpret_cast<u32x4_t*>(Vs + r * Sh::kVStride + c8 * 8) = vreg[i];
+      *reinterpret_cast<u32x4_t*>(dst + r * STRIDE + c8 * 8) = reg[i];
     }
   }
 }
@@ -161,83 +158,104 @@ __device__ __forceinline__ void softmax_prep(float* part, float scale_log2, int 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-template <int D, int BLK, int KT, int MODE>
-__global__ void __launch_bounds__(64 * (BLK / 32), 2) wise_attn_kernel(AttnParams p) {
-  using Sh = AttnShape<D, BLK, KT>;
+template <int D, int BLK, int KT, int MODE, int RPW>
+__global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(AttnParams p) {
+  using Sh = AttnShape<D, BLK, KT, RPW>;
+  using St = AttnShape<D, BLK, KT>;
+  constexpr int WR = BLK / 32;                 // waves per row
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);
   uint16_t* Vs = Ks + KT * Sh::kKsStride;
-  int32_t* blist = reinterpret_cast<int32_t*>(Vs + KT * Sh::kVStride);   // kSparse: [nblk + 1]
-  float* part = reinterpret_cast<float*>(Vs + KT * Sh::kVStride);       // kDenseMass: [nblk][BLK+1]
-  float* invl = part + (size_t)p.nblk * (BLK + 1);                      // kDenseMass: [BLK]
+  unsigned char* extra = smem + Sh::kTileLds;
+  const int nwords = (p.nblk + 31) / 32;
+  uint32_t* bits = reinterpret_cast<uint32_t*>(extra);                  // kSparse: [RPW][nwords]
+  int32_t* ulist = reinterpret_cast<int32_t*>(bits + RPW * nwords);     // kSparse: [nblk + 1]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int n = lane & 31;  // query within the wave; also key row within a 32-key MFMA tile
   const int g = lane >> 5;  // lane half
+  const int slot = wave / WR;   // which of the workgroup's rows this wave serves
+  const int wr = wave % WR;
 
-  // Longest rows first: blockIdx.x runs over query blocks from the last one.
+  // Longest rows first: blockIdx.x runs over row groups from the last one,
+  // (batch*head) inner.
+  const int n_groups = (p.nblk + RPW - 1) / RPW;
   const int L = blockIdx.x;
-  const int qb = p.nblk - 1 - L / p.heads_total;
+  const int grp = n_groups - 1 - L / p.heads_total;
   const int bh = L % p.heads_total;
+  const int q_lo = grp * RPW;
+  const int q_hi = min(q_lo + RPW - 1, p.nblk - 1);
+  const int qb = q_lo + slot;           // this wave's query block
+  const bool row_ok = qb < p.nblk;
   const int row = bh * p.nblk + qb;
+
+  float* part = reinterpret_cast<float*>(extra) + (size_t)slot * ((size_t)p.nblk * (BLK + 1) + BLK);
+  float* invl = part + (size_t)p.nblk * (BLK + 1);                        // kDenseMass
 
   const size_t head_off = (size_t)bh * p.seq * D;
   const uint16_t* Qh = p.q + head_off;
   const uint16_t* Kh = p.k + head_off;
   const uint16_t* Vh = p.v + head_off;
-  const int qrow = qb * BLK + wave * 32 + n;
+  const int qrow = qb * BLK + wr * 32 + n;
 
   bf16x8_t qf[Sh::kChunks];
 #pragma unroll
   for (int c = 0; c < Sh::kChunks; ++c)
-    qf[c] = *reinterpret_cast<const bf16x8_t*>(Qh + (size_t)qrow * D + c * 16 + 8 * g);
+    qf[c] = row_ok ? *reinterpret_cast<const bf16x8_t*>(Qh + (size_t)qrow * D + c * 16 + 8 * g)
+                   : bf16x8_t{};
 
-  // Key blocks of this row.  Dense: 0..qb.  Sparse: the CSR row, compacted
-  // into LDS by wave 0; entries out of [0, qb], repeated or not ascending
-  // are dropped, so every listed block is read once and the diagonal block,
-  // if listed, is last.
-  int n_blk = qb + 1;
-  bool has_diag = true;
+  // Key blocks walked by the workgroup: the union of its rows' lists, in
+  // ascending order, each entry tagged with the rows that list it.  Dense:
+  // 0..q_hi, row `slot` lists kb <= its query block.  Sparse: each row's CSR
+  // entries within [0, q] are ORed into an LDS bitmap (repeats count once,
+  // order does not matter), then wave 0 compacts the union with ballots.
+  int n_ent = q_hi + 1;
   if constexpr (MODE == kSparse) {
-    if (wave == 0) {
+    for (int i = tid; i < RPW * nwords; i += Sh::kThreads) bits[i] = 0u;
+    __syncthreads();
+    if (wr == 0 && row_ok) {
       int e_begin = p.row_ptr[row];
       int e_end = p.row_ptr[row + 1];
       if (e_end < e_begin) e_end = e_begin;
-      int carry = -1, count = 0;
-      for (int base = e_begin; base < e_end; base += 64) {
-        const int idx = base + lane;
-        const int c = idx < e_end ? p.col_idx[idx] : -1;
-        const bool inr = idx < e_end && c >= 0 && c <= qb;
-        int incl = inr ? c : -1;  // inclusive prefix max over lanes
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const int y = __shfl_up(incl, off);
-          if (lane >= off) incl = max(incl, y);
-        }
-        int excl = __shfl_up(incl, 1);
-        if (lane == 0) excl = -1;
-        excl = max(excl, carry);
-        const bool acc = inr && c > excl;
-        const uint64_t bal = __ballot(acc);
-        if (acc) blist[1 + count + __popcll(bal & ((1ull << lane) - 1ull))] = c;
-        count += __popcll(bal);
-        carry = max(carry, __shfl(incl, 63));
+      for (int idx = e_begin + lane; idx < e_end; idx += 64) {
+        const int c = p.col_idx[idx];
+        if (c >= 0 && c <= qb) atomicOr(&bits[slot * nwords + (c >> 5)], 1u << (c & 31));
       }
-      if (lane == 0) blist[0] = count;
     }
     __syncthreads();
-    n_blk = __builtin_amdgcn_readfirstlane(blist[0]);
-    has_diag = n_blk > 0 && __builtin_amdgcn_readfirstlane(blist[n_blk]) == qb;
+    if (wave == 0) {
+      int count = 0;
+      for (int base = 0; base <= q_hi; base += 64) {
+        const int c = base + lane;
+        uint32_t tag = 0;
+        if (c <= q_hi) {
+#pragma unroll
+          for (int r = 0; r < RPW; ++r) tag |= ((bits[r * nwords + (c >> 5)] >> (c & 31)) & 1u) << (29 + r);
+        }
+        const uint64_t bal = __ballot(tag != 0);
+        if (tag != 0) ulist[1 + count + __popcll(bal & ((1ull << lane) - 1ull))] = (int)(tag | (uint32_t)c);
+        count += __popcll(bal);
+      }
+      if (lane == 0) ulist[0] = count;
+    }
+    __syncthreads();
+    n_ent = __builtin_amdgcn_readfirstlane(ulist[0]);
   }
-  auto block_of = [&](int e) -> int {
-    if constexpr (MODE == kSparse) return __builtin_amdgcn_readfirstlane(blist[1 + e]);
-    else return e;
+  // Entry e -> (key block, does this wave's row list it).
+  auto entry = [&](int e, int& kb, bool& mine) {
+    if constexpr (MODE == kSparse) {
+      const uint32_t code = (uint32_t)__builtin_amdgcn_readfirstlane(ulist[1 + e]);
+      kb = (int)(code & 0x1FFFFFFFu);
+      mine = row_ok && ((code >> (29 + slot)) & 1u);
+    } else {
+      kb = e;
+      mine = row_ok && e <= qb;
+    }
   };
-  const int n_tiles = n_blk * Sh::kSub;
-  const int n_main = (n_blk - (has_diag ? 1 : 0)) * Sh::kSub;  // tiles without masking
+  const int n_tiles = n_ent * Sh::kSub;
 
   f32x16_t oacc[Sh::kDTiles];
 #pragma unroll
@@ -265,23 +283,16 @@ __global__ void __launch_bounds__(64 * (BLK / 32), 2) wise_attn_kernel(AttnParam
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Vh), 0, head_bytes, 0x00020000);
 
-  if (n_tiles > 0) load_tile<D, BLK, KT>(krs, vrs, block_of(0) * BLK, tid, kreg, vreg);
+  auto tile_key0 = [&](int it) {
+    int kb;
+    bool mine;
+    entry(it / Sh::kSub, kb, mine);
+    return kb * BLK + (it % Sh::kSub) * KT;
+  };
 
-  // One pipeline step: publish the prefetched tile, prefetch the next one,
-  // then compute on the published tile.
-  auto step = [&]<bool MASKED>(int it) __attribute__((always_inline)) {
-    const int sub = it % Sh::kSub;
-    const int kb = block_of(it / Sh::kSub);
+  // One tile for this wave's row: S^T = K Q^T, softmax, O^T += V^T P^T.
+  auto compute_tile = [&]<bool MASKED>(int kb, int sub) __attribute__((always_inline)) {
     const int key0 = kb * BLK + sub * KT;
-
-    __syncthreads();  // previous tile fully consumed
-    store_tile<D, BLK, KT>(Ks, Vs, tid, kreg, vreg);
-    __syncthreads();
-    if (it + 1 < n_tiles)
-      load_tile<D, BLK, KT>(krs, vrs, block_of((it + 1) / Sh::kSub) * BLK + ((it + 1) % Sh::kSub) * KT,
-                            tid, kreg, vreg);
-
-    // S^T = K Q^T
     f32x16_t s[Sh::kM];
 #pragma unroll
     for (int m = 0; m < Sh::kM; ++m) {
@@ -294,8 +305,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32), 2) wise_attn_kernel(AttnParam
         s[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[m], 0, 0, 0);
       }
     }
-
-    softmax_prep<D, BLK, KT, MODE, MASKED>(part, p.scale_log2, qrow - key0, g, n, wave, kb, m_ref,
+    softmax_prep<D, BLK, KT, MODE, MASKED>(part, p.scale_log2, qrow - key0, g, n, wr, kb, m_ref,
                                            l_part, blk_part, s, oacc);
 
     // P = exp2(s * scale*log2e - m) per 32-key sub-tile, then that
@@ -341,62 +351,91 @@ __global__ void __launch_bounds__(64 * (BLK / 32), 2) wise_attn_kernel(AttnParam
         }
     }
     l_part += tsum;
-    if constexpr (MODE == kDenseMass) blk_part += tsum;
-
     if constexpr (MODE == kDenseMass) {
+      blk_part += tsum;
       if (sub == Sh::kSub - 1) {
         const float bp = blk_part + __shfl_xor(blk_part, 32);
-        if (g == 0) part[kb * (BLK + 1) + wave * 32 + n] = bp;
+        if (g == 0) part[kb * (BLK + 1) + wr * 32 + n] = bp;
         blk_part = 0.f;
       }
     }
   };
 
-  int it = 0;
-  for (; it < n_main; ++it) step.template operator()<false>(it);
-  for (; it < n_tiles; ++it) step.template operator()<true>(it);
+  // Publish the prefetched tile, prefetch the next one, then every wave whose
+  // row lists the block computes on it (the causal mask only in the row's
+  // own diagonal block; the branches are wave-uniform).
+  if (n_tiles > 0) {
+    load_rows<D, BLK, KT, RPW>(krs, tile_key0(0), tid, kreg);
+    load_rows<D, BLK, KT, RPW>(vrs, tile_key0(0), tid, vreg);
+  }
+  for (int it = 0; it < n_tiles; ++it) {
+    int kb;
+    bool mine;
+    entry(it / Sh::kSub, kb, mine);
+    const int sub = it % Sh::kSub;
+    __syncthreads();  // previous tile fully consumed
+    store_rows<D, BLK, KT, RPW, Sh::kKsStride>(Ks, tid, kreg);
+    store_rows<D, BLK, KT, RPW, Sh::kVStride>(Vs, tid, vreg);
+    __syncthreads();
+    if (it + 1 < n_tiles) {
+      const int nk = tile_key0(it + 1);
+      load_rows<D, BLK, KT, RPW>(krs, nk, tid, kreg);
+      load_rows<D, BLK, KT, RPW>(vrs, nk, tid, vreg);
+    }
+    if (mine) {
+      if (kb == qb) compute_tile.template operator()<true>(kb, sub);
+      else compute_tile.template operator()<false>(kb, sub);
+    }
+  }
 
   // ---- epilogue -----------------------------------------------------------
   const float lt = l_part + __shfl_xor(l_part, 32);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  uint16_t* Oh = p.o + head_off + (size_t)qrow * D;
+  if (row_ok) {
+    uint16_t* Oh = p.o + head_off + (size_t)qrow * D;
 #pragma unroll
-  for (int t = 0; t < Sh::kDTiles; ++t)
+    for (int t = 0; t < Sh::kDTiles; ++t)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      __bf16 b0 = (__bf16)(oacc[t][4 * j + 0] * inv);
-      __bf16 b1 = (__bf16)(oacc[t][4 * j + 1] * inv);
-      __bf16 b2 = (__bf16)(oacc[t][4 * j + 2] * inv);
-      __bf16 b3 = (__bf16)(oacc[t][4 * j + 3] * inv);
-      u32x2_t w;
-      w.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-      w.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-      *reinterpret_cast<u32x2_t*>(Oh + t * 32 + 8 * j + 4 * g) = w;
+      for (int j = 0; j < 4; ++j) {
+        __bf16 b0 = (__bf16)(oacc[t][4 * j + 0] * inv);
+        __bf16 b1 = (__bf16)(oacc[t][4 * j + 1] * inv);
+        __bf16 b2 = (__bf16)(oacc[t][4 * j + 2] * inv);
+        __bf16 b3 = (__bf16)(oacc[t][4 * j + 3] * inv);
+        u32x2_t w;
+        w.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+        w.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+        *reinterpret_cast<u32x2_t*>(Oh + t * 32 + 8 * j + 4 * g) = w;
+      }
+    if (MODE == kDense && p.lse != nullptr && g == 0) {
+      const float lse = (lt > 0.f) ? (m_ref + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
+      p.lse[(size_t)bh * p.seq + qrow] = lse;
     }
-
-  if (MODE == kDense && p.lse != nullptr && g == 0) {
-    const float lse = (lt > 0.f) ? (m_ref + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
-    p.lse[(size_t)bh * p.seq + qrow] = lse;
   }
 
   if constexpr (MODE == kDenseMass) {
-    if (g == 0) invl[wave * 32 + n] = inv;
+    if (row_ok && g == 0) invl[wr * 32 + n] = inv;
     __syncthreads();
-    float* mrow = p.mass + (size_t)row * p.nblk;
-    for (int b = tid; b <= qb; b += Sh::kThreads) {
-      const float* pr = part + b * (BLK + 1);
+    // Row slot r's masses: r_qb = (1/B) sum_i partial_ib / l_i, one
+    // sequential sum per key block (deterministic).
+    for (int w = tid; w < RPW * p.nblk; w += Sh::kThreads) {
+      const int r = w / p.nblk, b = w % p.nblk;
+      const int qr = q_lo + r;
+      if (qr >= p.nblk || b > qr) continue;
+      const float* pr = reinterpret_cast<float*>(extra) + (size_t)r * ((size_t)p.nblk * (BLK + 1) + BLK);
+      const float* il = pr + (size_t)p.nblk * (BLK + 1);
+      pr += b * (BLK + 1);
       float acc = 0.f;
-      for (int i = 0; i < BLK; ++i) acc = fmaf(pr[i], invl[i], acc);
-      mrow[b] += acc * (1.0f / BLK);
+      for (int i = 0; i < BLK; ++i) acc = fmaf(pr[i], il[i], acc);
+      p.mass[((size_t)bh * p.nblk + qr) * p.nblk + b] += acc * (1.0f / BLK);
     }
   }
 }
 
-template <int D, int BLK, int KT, int MODE>
+template <int D, int BLK, int KT, int MODE, int RPW>
 hipError_t launch_attn_t(const AttnParams& p, hipStream_t stream) {
-  using Sh = AttnShape<D, BLK, KT>;
-  const size_t lds = attn_lds_need<D, BLK, KT>(MODE, p.nblk);
-  auto kern = wise_attn_kernel<D, BLK, KT, MODE>;
+  using Sh = AttnShape<D, BLK, KT, RPW>;
+  const size_t lds = attn_lds_need<D, BLK, KT, RPW>(MODE, p.nblk);
+  auto kern = wise_attn_kernel<D, BLK, KT, MODE, RPW>;
   static bool attr_set = false;  // benign race: idempotent attribute
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -404,61 +443,103 @@ hipError_t launch_attn_t(const AttnParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const unsigned grid = (unsigned)p.heads_total * (unsigned)p.nblk;
+  const unsigned grid = (unsigned)p.heads_total * (unsigned)((p.nblk + RPW - 1) / RPW);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(Sh::kThreads), lds, stream, p);
   return hipGetLastError();
 }
 
-// Key tile: 64 keys when it fits; the mass mode at long contexts drops to
-// 32 keys so that the per-(query, block) partials still fit in LDS.
+// Launch shape: keys per tile and rows per workgroup.
+struct AttnCfg {
+  int kt;
+  int rpw;
+};
+
 template <int D, int BLK>
-int choose_kt(int mode, int nblk) {
-  if constexpr (BLK == 32) {
-    return attn_lds_need<D, 32, 32>(mode, nblk) <= kMaxLds ? 32 : 0;
-  } else if constexpr (BLK == 64 && D == 128) {
-    // The mass mode's extra live state does not fit 64-key tiles in 256 VGPRs.
-    if (mode != kDenseMass && attn_lds_need<D, BLK, 64>(mode, nblk) <= kMaxLds) return 64;
-    if (attn_lds_need<D, BLK, 32>(mode, nblk) <= kMaxLds) return 32;
-    return 0;
+size_t cfg_lds(int kt, int rpw, int mode, int nblk) {
+  if constexpr (BLK >= 64) {
+    if (kt == 64 && rpw == 1) return attn_lds_need<D, BLK, 64, 1>(mode, nblk);
+    if (kt == 64 && rpw == 2) return attn_lds_need<D, BLK, 64, 2>(mode, nblk);
+  }
+  if (kt == 32 && rpw == 1) return attn_lds_need<D, BLK, 32, 1>(mode, nblk);
+  if (kt == 32 && rpw == 2) return attn_lds_need<D, BLK, 32, 2>(mode, nblk);
+  return 0;
+}
+
+#ifndef WISE_SPARSE_RPW64
+#define WISE_SPARSE_RPW64 2
+#endif
+
+// Dense and sparse launches: 64-key tiles (32 for block 32), two rows per
+// workgroup for block 64.  Mass launches: the candidate with the most
+// resident waves per CU under the LDS budget (two 2-wave rows, or one row;
+// 64- or 32-key tiles), preferring two rows and larger tiles on ties.
+template <int D, int BLK>
+AttnCfg choose_cfg(int mode, int nblk) {
+  constexpr int kWavesPerRow = BLK / 32;
+  if (mode != kDenseMass) {
+    const AttnCfg c{BLK >= 64 ? 64 : 32, BLK == 64 ? (mode == kSparse ? WISE_SPARSE_RPW64 : 2) : 1};
+    return cfg_lds<D, BLK>(c.kt, c.rpw, mode, nblk) <= kMaxLds ? c : AttnCfg{0, 0};
+  }
+  // (head_dim 128 at block 64 with 64-key tiles spills registers in this mode)
+  AttnCfg cands[4];
+  int nc = 0;
+  if (BLK == 64 && D != 128) cands[nc++] = {64, 2};
+  if (BLK == 64) cands[nc++] = {32, 2};
+  if (BLK >= 64 && !(BLK == 64 && D == 128)) cands[nc++] = {64, 1};
+  cands[nc++] = {32, 1};
+  AttnCfg best{0, 0};
+  int best_waves = 0;
+  for (int i = 0; i < nc; ++i) {
+    const size_t lds = cfg_lds<D, BLK>(cands[i].kt, cands[i].rpw, mode, nblk);
+    if (lds == 0 || lds > kMaxLds) continue;
+    const int waves = std::min((int)(kMaxLds / lds) * kWavesPerRow * cands[i].rpw, 8);
+    if (waves > best_waves) { best = cands[i]; best_waves = waves; }
+  }
+  return best;
+}
+
+template <int D, int BLK, int MODE>
+hipError_t launch_cfg(AttnCfg c, const AttnParams& p, hipStream_t stream) {
+  if constexpr (MODE != kDenseMass) {
+    if constexpr (BLK == 64) return launch_attn_t<D, 64, 64, MODE, MODE == kSparse ? WISE_SPARSE_RPW64 : 2>(p, stream);
+    else if constexpr (BLK == 128) return launch_attn_t<D, 128, 64, MODE, 1>(p, stream);
+    else return launch_attn_t<D, 32, 32, MODE, 1>(p, stream);
   } else {
-    if (attn_lds_need<D, BLK, 64>(mode, nblk) <= kMaxLds) return 64;
-    if (attn_lds_need<D, BLK, 32>(mode, nblk) <= kMaxLds) return 32;
-    return 0;
+    if constexpr (BLK == 64) {
+      if constexpr (D != 128) {
+        if (c.kt == 64 && c.rpw == 2) return launch_attn_t<D, 64, 64, MODE, 2>(p, stream);
+        if (c.kt == 64 && c.rpw == 1) return launch_attn_t<D, 64, 64, MODE, 1>(p, stream);
+      }
+      if (c.kt == 32 && c.rpw == 2) return launch_attn_t<D, 64, 32, MODE, 2>(p, stream);
+      if (c.kt == 32 && c.rpw == 1) return launch_attn_t<D, 64, 32, MODE, 1>(p, stream);
+      return hipErrorInvalidValue;
+    } else if constexpr (BLK == 128) {
+      if (c.kt == 64) return launch_attn_t<D, 128, 64, MODE, 1>(p, stream);
+      return launch_attn_t<D, 128, 32, MODE, 1>(p, stream);
+    } else {
+      return launch_attn_t<D, 32, 32, MODE, 1>(p, stream);
+    }
   }
 }
 
 template <int D, int BLK>
 hipError_t launch_attn_blk(int mode, const AttnParams& p, hipStream_t stream) {
-  const int kt = choose_kt<D, BLK>(mode, p.nblk);
-  if (kt == 0) return hipErrorInvalidValue;
-  if constexpr (BLK == 32) {
-    switch (mode) {
-      case kDense: return launch_attn_t<D, BLK, 32, kDense>(p, stream);
-      case kDenseMass: return launch_attn_t<D, BLK, 32, kDenseMass>(p, stream);
-      default: return launch_attn_t<D, BLK, 32, kSparse>(p, stream);
-    }
-  } else {
-    if (mode == kDense) return launch_attn_t<D, BLK, 64, kDense>(p, stream);
-    if (mode == kSparse) return launch_attn_t<D, BLK, 64, kSparse>(p, stream);
-    if (kt == 64) return launch_attn_t<D, BLK, 64, kDenseMass>(p, stream);
-    return launch_attn_t<D, BLK, 32, kDenseMass>(p, stream);
+  const AttnCfg c = choose_cfg<D, BLK>(mode, p.nblk);
+  if (c.kt == 0) return hipErrorInvalidValue;
+  switch (mode) {
+    case kDense: return launch_cfg<D, BLK, kDense>(c, p, stream);
+    case kSparse: return launch_cfg<D, BLK, kSparse>(c, p, stream);
+    default: return launch_cfg<D, BLK, kDenseMass>(c, p, stream);
   }
 }
 
 template <int D>
 size_t attn_lds_bytes_d(int block, int mode, int nblk) {
+  AttnCfg c{0, 0};
   switch (block) {
-    case 32: return choose_kt<D, 32>(mode, nblk) ? attn_lds_need<D, 32, 32>(mode, nblk) : 0;
-    case 64: {
-      int kt = choose_kt<D, 64>(mode, nblk);
-      return kt == 64 ? attn_lds_need<D, 64, 64>(mode, nblk)
-                      : (kt == 32 ? attn_lds_need<D, 64, 32>(mode, nblk) : 0);
-    }
-    case 128: {
-      int kt = choose_kt<D, 128>(mode, nblk);
-      return kt == 64 ? attn_lds_need<D, 128, 64>(mode, nblk)
-                      : (kt == 32 ? attn_lds_need<D, 128, 32>(mode, nblk) : 0);
-    }
+    case 32: c = choose_cfg<D, 32>(mode, nblk); return c.kt ? cfg_lds<D, 32>(c.kt, c.rpw, mode, nblk) : 0;
+    case 64: c = choose_cfg<D, 64>(mode, nblk); return c.kt ? cfg_lds<D, 64>(c.kt, c.rpw, mode, nblk) : 0;
+    case 128: c = choose_cfg<D, 128>(mode, nblk); return c.kt ? cfg_lds<D, 128>(c.kt, c.rpw, mode, nblk) : 0;
   }
   return 0;
 }

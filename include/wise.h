@@ -124,10 +124,12 @@ wise_status_t wise_select_support(const wise_attn_desc_t* desc, const float* mas
  * the causal mask applies inside the diagonal block.
  *
  * q, k, v, o: as in wise_full_attn.
- * row_ptr, col_idx: CSR over rows (as written by wise_select_support).  Each
- *          row must list distinct blocks in ascending order, all <= q.  A row
- *          whose listed blocks hold no admissible key for some query yields
- *          zeros for that query.
+ * row_ptr, col_idx: CSR over rows (as written by wise_select_support).  A
+ *          row's entries are read as a set of key blocks: entries outside
+ *          [0, q] are ignored, repeated entries count once and their order
+ *          does not matter.  A query with no admissible key in its row's
+ *          blocks gets a zero output.  col_idx must hold row_ptr[n_rows]
+ *          readable entries.
  */
 wise_status_t wise_sparse_attn(const wise_attn_desc_t* desc, const void* q, const void* k,
                                const void* v, const int32_t* row_ptr, const int32_t* col_idx,
