@@ -180,12 +180,30 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   const int slot = wave / WR;   // which of the workgroup's rows this wave serves
   const int wr = wave % WR;
 
-  // Longest rows first: blockIdx.x runs over row groups from the last one,
-  // (batch*head) inner.
+  // Workgroup -> (head, row group).  Workgroups are dealt round-robin to the
+  // eight XCDs, each with its own L2.  With head_chunk > 0 (heads_total a
+  // multiple of 8), the workgroups with blockIdx % 8 == x serve heads
+  // [x*hpx, (x+1)*hpx) only, taken in chunks of head_chunk heads; inside a
+  // chunk, longest row groups first with the chunk's heads interleaved.  A
+  // chunk of all hpx heads is plain longest-first order; smaller chunks keep
+  // fewer heads' K/V in flight per L2.  head_chunk == 0: longest first over
+  // all heads.
   const int n_groups = (p.nblk + RPW - 1) / RPW;
-  const int L = blockIdx.x;
-  const int grp = n_groups - 1 - L / p.heads_total;
-  const int bh = L % p.heads_total;
+  int grp, bh;
+  if (p.head_chunk > 0) {
+    const int x = blockIdx.x & 7;
+    const int j = blockIdx.x >> 3;
+    const int hpx = p.heads_total >> 3;
+    const int per_chunk = p.head_chunk * n_groups;
+    const int c = j / per_chunk;
+    const int r = j - c * per_chunk;
+    const int hc = min(p.head_chunk, hpx - c * p.head_chunk);
+    grp = n_groups - 1 - r / hc;
+    bh = x * hpx + c * p.head_chunk + r % hc;
+  } else {
+    grp = n_groups - 1 - (int)blockIdx.x / p.heads_total;
+    bh = (int)blockIdx.x % p.heads_total;
+  }
   const int q_lo = grp * RPW;
   const int q_hi = min(q_lo + RPW - 1, p.nblk - 1);
   const int qb = q_lo + slot;           // this wave's query block
@@ -431,19 +449,45 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   }
 }
 
+// Heads per chunk for the workgroup order (see the kernel prologue).  When
+// one XCD's workgroups are at most four times its resident slots, plain
+// longest-first order over its heads keeps the tail short; above that,
+// chunks of about two slot-fills keep few heads' K/V per L2.  Needs
+// heads_total % 8 == 0 (each head then stays on one XCD).
+inline int choose_head_chunk(int heads_total, int n_groups, int wgs_per_cu) {
+  if (heads_total % 8 != 0) return 0;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+    return 0;
+  const int hpx = heads_total / 8;
+  const long slots = (long)wgs_per_cu * (cus / 8);
+  if ((long)hpx * n_groups <= 4 * slots) return hpx;
+  const long hc = (2 * slots + n_groups - 1) / n_groups;
+  return (int)std::max(1L, std::min<long>(hc, hpx));
+}
+
 template <int D, int BLK, int KT, int MODE, int RPW>
-hipError_t launch_attn_t(const AttnParams& p, hipStream_t stream) {
+hipError_t launch_attn_t(const AttnParams& p_in, hipStream_t stream) {
   using Sh = AttnShape<D, BLK, KT, RPW>;
-  const size_t lds = attn_lds_need<D, BLK, KT, RPW>(MODE, p.nblk);
+  const size_t lds = attn_lds_need<D, BLK, KT, RPW>(MODE, p_in.nblk);
   auto kern = wise_attn_kernel<D, BLK, KT, MODE, RPW>;
-  static bool attr_set = false;  // benign race: idempotent attribute
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  const unsigned grid = (unsigned)p.heads_total * (unsigned)((p.nblk + RPW - 1) / RPW);
+  // Once per process: allow the full LDS budget and read how many
+  // workgroups fit one CU by registers alone (thread-safe static init).
+  static const int regs_wgs = [&]() -> int {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds) != hipSuccess)
+      return -1;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, Sh::kThreads, 0) != hipSuccess) return -1;
+    return n;
+  }();
+  if (regs_wgs < 0) return hipErrorInvalidDeviceFunction;
+  AttnParams p = p_in;
+  const int n_groups = (p.nblk + RPW - 1) / RPW;
+  p.head_chunk = choose_head_chunk(p.heads_total, n_groups,
+                                   std::max(1, std::min(regs_wgs, (int)(kMaxLds / std::max<size_t>(lds, 1)))));
+  const unsigned grid = (unsigned)p.heads_total * (unsigned)n_groups;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(Sh::kThreads), lds, stream, p);
   return hipGetLastError();
 }

@@ -27,6 +27,7 @@ struct AttnParams {
   int32_t seq;
   int32_t nblk;            // seq / block
   float scale_log2;        // softmax scale * log2(e)
+  int32_t head_chunk;      // workgroup order (set by the launcher): 0, or heads per chunk within an XCD
 };
 
 struct AttnLaunch {
