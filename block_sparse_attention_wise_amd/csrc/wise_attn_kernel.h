@@ -46,6 +46,45 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads it
+// does not wait for outstanding global->LDS loads, which the caller waits
+// for explicitly (s_waitcnt vmcnt) when it needs them.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// s_waitcnt immediate: vmcnt <= 0, expcnt and lgkmcnt not waited for.
+constexpr int kWaitVm0 = 0x0F70;
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over `bytes` bytes at `base` (word 3: 32-bit raw
+// data format, no swizzle).
+__device__ __forceinline__ i32x4_t buffer_desc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_t d;
+  d.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  d.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
+  d.z = (int)bytes;
+  d.w = 0x00020000;
+  return d;
+}
+
+// 16 bytes per lane from buffer offset voff + soff straight into LDS at
+// lds_base + 16 * lane (buffer_load_dwordx4 ... lds; M0 holds the LDS base).
+// Written as inline assembly so that the compiler does not track these
+// LDS writes: completion is waited for explicitly (s_waitcnt vmcnt before
+// the barrier that publishes a stage), and LDS reads of the other stage
+// need not wait for them.
+__device__ __forceinline__ void dma16(i32x4_t desc, uint32_t lds_base, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(desc), "s"(soff)
+               : "memory", "m0");
+}
+
 template <int D, int BLK, int KT, int RPW = 1>
 struct AttnShape {
   static constexpr int kWaves = BLK / 32 * RPW;   // RPW rows of BLK queries per workgroup
@@ -68,13 +107,49 @@ struct AttnShape {
   static_assert(kVChunks % 16 == 4 || kVChunks % 16 == 12, "V stride");
 };
 
+// K/V tiles written straight from global memory into LDS
+// (buffer_load_dwordx4 ... lds): one wave instruction fills 1 KiB of LDS
+// contiguously (lane l at +16 l), so rows are unpadded (2D bytes) and bank
+// conflicts are avoided by permuting the 16-byte chunks of each row with an
+// XOR of row-index bits instead; the permutation is undone on the global
+// side of the load, so every lane still reads 16 contiguous bytes.  Two
+// stages: the tile after the current one lands while the current one is
+// used.
+//   K (read as the A operand, 16 rows x one chunk per pass):
+//     D=128: chunk ^ (r & 15); D=96: chunk ^ ((r >> 2) & 3); D=64: chunk ^ ((r >> 1) & 7)
+//   V (read transposed, 4 rows x 4 chunks per pass):
+//     D=128: chunk ^ 4(r & 3);  D=96: identity;            D=64: chunk ^ 4((r >> 1) & 1)
+// Both depend on r mod 32 only for K and r mod 8 only for V, so the row
+// offsets of the MFMA sub-tiles stay compile-time immediates.
+template <int D, int KT, int NT>
+struct DmaTile {
+  static constexpr int kCpr = D / 8;                          // 16-byte chunks per row
+  static constexpr int kTileBytes = KT * D * 2;               // one of K or V
+  static constexpr int kStageBytes = 2 * kTileBytes;
+  static constexpr int kStages = 2;
+  static constexpr int kWaves = NT / 64;
+  static constexpr int kInstr = KT * kCpr / 64 / kWaves;      // per wave and tensor
+  static constexpr bool kSplits = (KT * kCpr) % (64 * kWaves) == 0;  // whole wave loads
+  static __device__ __forceinline__ int kx(int r) {
+    return D == 128 ? (r & 15) : D == 96 ? ((r >> 2) & 3) : ((r >> 1) & 7);
+  }
+  static __device__ __forceinline__ int vx(int r) {
+    return D == 128 ? 4 * (r & 3) : D == 96 ? 0 : 4 * ((r >> 1) & 1);
+  }
+};
+
+template <int MODE>
+__host__ __device__ constexpr bool uses_dma() { return MODE != kDenseMass; }
+
 // Rows (query blocks) per workgroup: two adjacent rows for block 64, so
 // that four waves share every staged K/V tile (the two rows' key-block
 // lists overlap heavily), one row otherwise.  The mass mode keeps one row
 // when the per-(query, key block) partials of two rows would not fit.
 template <int D, int BLK, int KT, int RPW>
 __host__ __device__ constexpr size_t attn_lds_need(int mode, int nblk) {
-  return AttnShape<D, BLK, KT, RPW>::kTileLds +
+  return (mode != kDenseMass ? (size_t)DmaTile<D, KT, AttnShape<D, BLK, KT, RPW>::kThreads>::kStages *
+                                   DmaTile<D, KT, AttnShape<D, BLK, KT, RPW>::kThreads>::kStageBytes
+                             : AttnShape<D, BLK, KT, RPW>::kTileLds) +
          (mode == kDenseMass ? (size_t)RPW * ((size_t)nblk * (BLK + 1) + BLK) * 4 : 0) +
          (mode == kSparse ? (size_t)RPW * ((nblk + 31) / 32) * 4 + ((size_t)nblk + 1) * 4 : 0);
 }
@@ -164,10 +239,14 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   using St = AttnShape<D, BLK, KT>;
   constexpr int WR = BLK / 32;                 // waves per row
 
+  using Dm = DmaTile<D, KT, Sh::kThreads>;
+  constexpr bool kDma = uses_dma<MODE>();
+  static_assert(!kDma || Dm::kSplits, "K/V tile must split into whole wave loads");
+
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);
   uint16_t* Vs = Ks + KT * Sh::kKsStride;
-  unsigned char* extra = smem + Sh::kTileLds;
+  unsigned char* extra = smem + (kDma ? (size_t)Dm::kStages * Dm::kStageBytes : Sh::kTileLds);
   const int nwords = (p.nblk + 31) / 32;
   uint32_t* bits = reinterpret_cast<uint32_t*>(extra);                  // kSparse: [RPW][nwords]
   int32_t* ulist = reinterpret_cast<int32_t*>(bits + RPW * nwords);     // kSparse: [nblk + 1]
@@ -294,6 +373,31 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   // consecutive keys at dim 16(G%2) + i, which is the A-operand layout.
   const int v_lane_off = (4 * g + ((lane & 15) >> 2)) * Sh::kVStride + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
+  // Direct-to-LDS staging (dense and sparse): per-lane read offsets into a
+  // stage (u16 elements) and per-lane global byte offsets of each wave
+  // load, both through the row-chunk permutations of DmaTile.
+  int koff[Sh::kChunks];
+  int voffs[Sh::kDTiles];
+  uint32_t dk[Dm::kInstr];
+  uint32_t dv[Dm::kInstr];
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  if constexpr (kDma) {
+#pragma unroll
+    for (int c = 0; c < Sh::kChunks; ++c) koff[c] = n * D + (((2 * c + g) ^ Dm::kx(n)) * 8);
+    const int vrow = 4 * g + ((lane & 15) >> 2);
+    const int lc0 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int t = 0; t < Sh::kDTiles; ++t)
+      voffs[t] = vrow * D + (((lc0 + 4 * t) ^ Dm::vx(vrow)) * 8) + 4 * (lane & 1);
+#pragma unroll
+    for (int i = 0; i < Dm::kInstr; ++i) {
+      const int ci = (i * Dm::kWaves + wave) * 64 + lane;
+      const int r = ci / Dm::kCpr, pc = ci % Dm::kCpr;
+      dk[i] = (uint32_t)(r * D * 2 + ((pc ^ Dm::kx(r)) * 16));
+      dv[i] = (uint32_t)(r * D * 2 + ((pc ^ Dm::vx(r)) * 16));
+    }
+  }
+
   // Buffer resources over this head's K and V (word 3: raw 32-bit data format).
   const int head_bytes = p.seq * D * 2;
   const __amdgpu_buffer_rsrc_t krs =
@@ -308,8 +412,24 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
     return kb * BLK + (it % Sh::kSub) * KT;
   };
 
+  // Issue this wave's share of one K/V tile into LDS stage `stage`.
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+  const i32x4_t kdesc = buffer_desc(Kh, (uint32_t)head_bytes);
+  const i32x4_t vdesc = buffer_desc(Vh, (uint32_t)head_bytes);
+  auto dma_tile = [&](int stage, int key0) __attribute__((always_inline)) {
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)key0 * D * 2);
+    const uint32_t kbase = __builtin_amdgcn_readfirstlane(lds0 + stage * Dm::kStageBytes + wave_u * 1024);
+#pragma unroll
+    for (int i = 0; i < Dm::kInstr; ++i) {
+      dma16(kdesc, kbase + i * Dm::kWaves * 1024, dk[i], soff);
+      dma16(vdesc, kbase + i * Dm::kWaves * 1024 + Dm::kTileBytes, dv[i], soff);
+    }
+  };
+
   // One tile for this wave's row: S^T = K Q^T, softmax, O^T += V^T P^T.
-  auto compute_tile = [&]<bool MASKED>(int kb, int sub) __attribute__((always_inline)) {
+  // Kt/Vt: the LDS stage holding the tile (direct-to-LDS staging).
+  auto compute_tile = [&]<bool MASKED>(int kb, int sub, const uint16_t* Kt,
+                                       const uint16_t* Vt) __attribute__((always_inline)) {
     const int key0 = kb * BLK + sub * KT;
     f32x16_t s[Sh::kM];
 #pragma unroll
@@ -318,8 +438,9 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
       for (int i = 0; i < 16; ++i) s[m][i] = 0.f;
 #pragma unroll
       for (int c = 0; c < Sh::kChunks; ++c) {
-        const bf16x8_t a =
-            *reinterpret_cast<const bf16x8_t*>(Ks + (m * 32 + n) * Sh::kKsStride + c * 16 + 8 * g);
+        const uint16_t* kp = kDma ? Kt + koff[c] + m * 32 * D
+                                  : Ks + (m * 32 + n) * Sh::kKsStride + c * 16 + 8 * g;
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kp);
         s[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[m], 0, 0, 0);
       }
     }
@@ -358,11 +479,13 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
       for (int t = 0; t < Sh::kDTiles; ++t)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const uint16_t* vp = Vs + v_lane_off + (32 * m + 16 * kk) * Sh::kVStride + 32 * t;
+          constexpr int kVRow = kDma ? D : Sh::kVStride;
+          const uint16_t* vp = kDma ? Vt + voffs[t] + (32 * m + 16 * kk) * D
+                                    : Vs + v_lane_off + (32 * m + 16 * kk) * Sh::kVStride + 32 * t;
           const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) i16x4_t*)(vp));
           const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4_t*)(vp + 8 * Sh::kVStride));
+              (__attribute__((address_space(3))) i16x4_t*)(vp + 8 * kVRow));
           const bf16x8_t a =
               __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], oacc[t], 0, 0, 0);
@@ -382,6 +505,28 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   // Publish the prefetched tile, prefetch the next one, then every wave whose
   // row lists the block computes on it (the causal mask only in the row's
   // own diagonal block; the branches are wave-uniform).
+  if constexpr (kDma) {
+    // Wait for this wave's loads of tile `it`, then one barrier: every
+    // wave's share has landed and every wave is done with the other stage,
+    // which then receives tile it+1 while tile it is used.
+    if (n_tiles > 0) dma_tile(0, tile_key0(0));
+    for (int it = 0; it < n_tiles; ++it) {
+      int kb;
+      bool mine;
+      entry(it / Sh::kSub, kb, mine);
+      const int sub = it % Sh::kSub;
+      const int st = it & 1;
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      lds_barrier();
+      if (it + 1 < n_tiles) dma_tile(st ^ 1, tile_key0(it + 1));
+      const uint16_t* Kt = reinterpret_cast<const uint16_t*>(smem + st * Dm::kStageBytes);
+      const uint16_t* Vt = Kt + KT * D;
+      if (mine) {
+        if (kb == qb) compute_tile.template operator()<true>(kb, sub, Kt, Vt);
+        else compute_tile.template operator()<false>(kb, sub, Kt, Vt);
+      }
+    }
+  } else {
   if (n_tiles > 0) {
     load_rows<D, BLK, KT, RPW>(krs, tile_key0(0), tid, kreg);
     load_rows<D, BLK, KT, RPW>(vrs, tile_key0(0), tid, vreg);
@@ -401,9 +546,10 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
       load_rows<D, BLK, KT, RPW>(vrs, nk, tid, vreg);
     }
     if (mine) {
-      if (kb == qb) compute_tile.template operator()<true>(kb, sub);
-      else compute_tile.template operator()<false>(kb, sub);
+      if (kb == qb) compute_tile.template operator()<true>(kb, sub, Ks, Vs);
+      else compute_tile.template operator()<false>(kb, sub, Ks, Vs);
     }
+  }
   }
 
   // ---- epilogue -----------------------------------------------------------
