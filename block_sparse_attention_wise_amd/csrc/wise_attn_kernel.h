@@ -1,19 +1,21 @@
 // Flash-style causal attention kernel for gfx950 (CDNA4), bf16 MFMA.
 //
-// One workgroup owns one row = (batch*head, query block q) of B = BLK
-// queries; wave w of the workgroup owns queries [q*B + 32w, q*B + 32w + 32).
-// The workgroup walks a list of key blocks (all of 0..q for the dense modes,
-// the CSR row for the sparse mode), KT keys at a time:
+// A workgroup owns RPW adjacent rows = (batch*head, query block q) of
+// B = BLK queries each; the waves of a row own 32 queries apiece.  The
+// workgroup walks a list of key blocks, KT keys at a time: all of 0..q for
+// the dense modes, the union of its rows' CSR lists for the sparse mode
+// (each wave computes only on blocks its own row lists):
 //
-//   global --(16-byte loads, prefetched one tile ahead into VGPRs)--> LDS
-//   S^T = K Q^T      v_mfma_f32_32x32x16_bf16, K tile from LDS, Q in VGPRs
+//   global --(buffer_load_dwordx4 ... lds, two stages)--> LDS
+//             (mass mode: 16-byte loads into VGPRs, then LDS stores)
+//   S^T = K Q^T      v_mfma_f32_32x32x16_bf16, K rows from LDS, Q in VGPRs
 //   P   = exp2(S^T * scale*log2e - m)   (fp32, lazily rescaled running max)
-//   O^T += V^T P^T   v_mfma_f32_32x32x16_bf16, V^T tile from LDS, P in VGPRs
+//   O^T += V^T P^T   v_mfma_f32_32x32x16_bf16, V^T read from row-major V
+//                    with ds_read_b64_tr_b16, P in VGPRs
 //
 // Computing the transposed score tile makes the MFMA accumulator layout of
 // S^T (lane = query, 16 keys per lane) coincide with the B-operand layout
-// the PV product needs, so P never leaves registers.  V is transposed on its
-// way into LDS (4 keys x 8 dims per thread, packed 8-byte LDS stores).
+// the PV product needs, so P never leaves registers.
 //
 // Softmax: the reference max m of a query is only raised when a new score
 // exceeds it by more than 2^kTau (in log2 units); otherwise P may grow up to
@@ -304,6 +306,51 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
     qf[c] = row_ok ? *reinterpret_cast<const bf16x8_t*>(Qh + (size_t)qrow * D + c * 16 + 8 * g)
                    : bf16x8_t{};
 
+  const int head_bytes = p.seq * D * 2;
+  // Direct-to-LDS staging (dense and sparse): per-lane read offsets into a
+  // stage (u16 elements) and per-lane global byte offsets of each wave
+  // load, both through the row-chunk permutations of DmaTile.
+  int koff[Sh::kChunks];
+  int voffs[Sh::kDTiles];
+  uint32_t dk[Dm::kInstr];
+  uint32_t dv[Dm::kInstr];
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  if constexpr (kDma) {
+#pragma unroll
+    for (int c = 0; c < Sh::kChunks; ++c) koff[c] = n * D + (((2 * c + g) ^ Dm::kx(n)) * 8);
+    const int vrow = 4 * g + ((lane & 15) >> 2);
+    const int lc0 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int t = 0; t < Sh::kDTiles; ++t)
+      voffs[t] = vrow * D + (((lc0 + 4 * t) ^ Dm::vx(vrow)) * 8) + 4 * (lane & 1);
+#pragma unroll
+    for (int i = 0; i < Dm::kInstr; ++i) {
+      const int ci = (i * Dm::kWaves + wave) * 64 + lane;
+      const int r = ci / Dm::kCpr, pc = ci % Dm::kCpr;
+      dk[i] = (uint32_t)(r * D * 2 + ((pc ^ Dm::kx(r)) * 16));
+      dv[i] = (uint32_t)(r * D * 2 + ((pc ^ Dm::vx(r)) * 16));
+    }
+  }
+
+  // Issue this wave's share of one K/V tile into LDS stage `stage`.
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+  const i32x4_t kdesc = buffer_desc(Kh, (uint32_t)head_bytes);
+  const i32x4_t vdesc = buffer_desc(Vh, (uint32_t)head_bytes);
+  auto dma_tile = [&](int stage, int key0) __attribute__((always_inline)) {
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)key0 * D * 2);
+    const uint32_t kbase = __builtin_amdgcn_readfirstlane(lds0 + stage * Dm::kStageBytes + wave_u * 1024);
+#pragma unroll
+    for (int i = 0; i < Dm::kInstr; ++i) {
+      dma16(kdesc, kbase + i * Dm::kWaves * 1024, dk[i], soff);
+      dma16(vdesc, kbase + i * Dm::kWaves * 1024 + Dm::kTileBytes, dv[i], soff);
+    }
+  };
+  // The first tile of every dense row and of every row the selection
+  // writes is key block 0 (the sink), so its load is issued now, before the
+  // list is known; the sparse prologue below re-issues it if the list
+  // starts elsewhere.
+  if constexpr (kDma) dma_tile(0, 0);
+
   // Key blocks walked by the workgroup: the union of its rows' lists, in
   // ascending order, each entry tagged with the rows that list it.  Dense:
   // 0..q_hi, row `slot` lists kb <= its query block.  Sparse: each row's CSR
@@ -312,7 +359,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   int n_ent = q_hi + 1;
   if constexpr (MODE == kSparse) {
     for (int i = tid; i < RPW * nwords; i += Sh::kThreads) bits[i] = 0u;
-    __syncthreads();
+    lds_barrier();
     if (wr == 0 && row_ok) {
       int e_begin = p.row_ptr[row];
       int e_end = p.row_ptr[row + 1];
@@ -322,7 +369,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
         if (c >= 0 && c <= qb) atomicOr(&bits[slot * nwords + (c >> 5)], 1u << (c & 31));
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) {
       int count = 0;
       for (int base = 0; base <= q_hi; base += 64) {
@@ -338,7 +385,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
       }
       if (lane == 0) ulist[0] = count;
     }
-    __syncthreads();
+    lds_barrier();
     n_ent = __builtin_amdgcn_readfirstlane(ulist[0]);
   }
   // Entry e -> (key block, does this wave's row list it).
@@ -373,33 +420,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   // consecutive keys at dim 16(G%2) + i, which is the A-operand layout.
   const int v_lane_off = (4 * g + ((lane & 15) >> 2)) * Sh::kVStride + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  // Direct-to-LDS staging (dense and sparse): per-lane read offsets into a
-  // stage (u16 elements) and per-lane global byte offsets of each wave
-  // load, both through the row-chunk permutations of DmaTile.
-  int koff[Sh::kChunks];
-  int voffs[Sh::kDTiles];
-  uint32_t dk[Dm::kInstr];
-  uint32_t dv[Dm::kInstr];
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  if constexpr (kDma) {
-#pragma unroll
-    for (int c = 0; c < Sh::kChunks; ++c) koff[c] = n * D + (((2 * c + g) ^ Dm::kx(n)) * 8);
-    const int vrow = 4 * g + ((lane & 15) >> 2);
-    const int lc0 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-#pragma unroll
-    for (int t = 0; t < Sh::kDTiles; ++t)
-      voffs[t] = vrow * D + (((lc0 + 4 * t) ^ Dm::vx(vrow)) * 8) + 4 * (lane & 1);
-#pragma unroll
-    for (int i = 0; i < Dm::kInstr; ++i) {
-      const int ci = (i * Dm::kWaves + wave) * 64 + lane;
-      const int r = ci / Dm::kCpr, pc = ci % Dm::kCpr;
-      dk[i] = (uint32_t)(r * D * 2 + ((pc ^ Dm::kx(r)) * 16));
-      dv[i] = (uint32_t)(r * D * 2 + ((pc ^ Dm::vx(r)) * 16));
-    }
-  }
-
   // Buffer resources over this head's K and V (word 3: raw 32-bit data format).
-  const int head_bytes = p.seq * D * 2;
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Kh), 0, head_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
@@ -411,45 +432,43 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
     entry(it / Sh::kSub, kb, mine);
     return kb * BLK + (it % Sh::kSub) * KT;
   };
-
-  // Issue this wave's share of one K/V tile into LDS stage `stage`.
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
-  const i32x4_t kdesc = buffer_desc(Kh, (uint32_t)head_bytes);
-  const i32x4_t vdesc = buffer_desc(Vh, (uint32_t)head_bytes);
-  auto dma_tile = [&](int stage, int key0) __attribute__((always_inline)) {
-    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)key0 * D * 2);
-    const uint32_t kbase = __builtin_amdgcn_readfirstlane(lds0 + stage * Dm::kStageBytes + wave_u * 1024);
-#pragma unroll
-    for (int i = 0; i < Dm::kInstr; ++i) {
-      dma16(kdesc, kbase + i * Dm::kWaves * 1024, dk[i], soff);
-      dma16(vdesc, kbase + i * Dm::kWaves * 1024 + Dm::kTileBytes, dv[i], soff);
+  if constexpr (MODE == kSparse) {
+    // The speculative first load was wrong (or is not needed): let it land,
+    // then load the list's first tile.  Nothing may still be writing this
+    // workgroup's LDS when it exits.
+    if (n_tiles == 0 || tile_key0(0) != 0) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      if (n_tiles > 0) dma_tile(0, tile_key0(0));
     }
-  };
+  }
 
-  // One tile for this wave's row: S^T = K Q^T, softmax, O^T += V^T P^T.
-  // Kt/Vt: the LDS stage holding the tile (direct-to-LDS staging).
-  auto compute_tile = [&]<bool MASKED>(int kb, int sub, const uint16_t* Kt,
-                                       const uint16_t* Vt) __attribute__((always_inline)) {
-    const int key0 = kb * BLK + sub * KT;
-    f32x16_t s[Sh::kM];
+  // S^T = K Q^T for one key tile (Kt: the LDS slot holding its K rows).
+  auto scores = [&](f32x16_t (&sc)[Sh::kM], const uint16_t* Kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < Sh::kM; ++m) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[m][i] = 0.f;
+      for (int i = 0; i < 16; ++i) sc[m][i] = 0.f;
 #pragma unroll
       for (int c = 0; c < Sh::kChunks; ++c) {
         const uint16_t* kp = kDma ? Kt + koff[c] + m * 32 * D
                                   : Ks + (m * 32 + n) * Sh::kKsStride + c * 16 + 8 * g;
         const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kp);
-        s[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[m], 0, 0, 0);
+        sc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], sc[m], 0, 0, 0);
       }
     }
-    softmax_prep<D, BLK, KT, MODE, MASKED>(part, p.scale_log2, qrow - key0, g, n, wr, kb, m_ref,
-                                           l_part, blk_part, s, oacc);
+  };
 
-    // P = exp2(s * scale*log2e - m) per 32-key sub-tile, then that
-    // sub-tile's O^T += V^T P^T; the exponentials of sub-tile m+1 are
-    // independent of the MFMAs of sub-tile m.  Masked scores are -inf -> 0.
+  // Causal mask (diagonal block only), lazy-rescale check and rare rescale.
+  auto prep = [&]<bool MASKED>(int kb, int sub, f32x16_t (&sc)[Sh::kM]) __attribute__((always_inline)) {
+    softmax_prep<D, BLK, KT, MODE, MASKED>(part, p.scale_log2, qrow - (kb * BLK + sub * KT), g, n, wr, kb,
+                                           m_ref, l_part, blk_part, sc, oacc);
+  };
+
+  // P = exp2(s * scale*log2e - m) per 32-key sub-tile, then that
+  // sub-tile's O^T += V^T P^T (Vt: the LDS slot holding the tile's V rows);
+  // the exponentials of sub-tile m+1 are independent of the MFMAs of
+  // sub-tile m.  Masked scores are -inf -> 0.
+  auto expv = [&](int kb, int sub, f32x16_t (&sc)[Sh::kM], const uint16_t* Vt) __attribute__((always_inline)) {
     const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
     float tsum = 0.f;
 #pragma unroll
@@ -459,7 +478,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(s[m][kk * 8 + e], p.scale_log2, neg_m));
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sc[m][kk * 8 + e], p.scale_log2, neg_m));
           if constexpr (MODE == kDenseMass) tsum += pv;   // block mass needs the fp32 values
           pf[kk][e] = (__bf16)pv;
         }
@@ -502,14 +521,23 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
     }
   };
 
+  // One whole tile for this wave's row.
+  auto compute_tile = [&]<bool MASKED>(int kb, int sub, const uint16_t* Kt,
+                                       const uint16_t* Vt) __attribute__((always_inline)) {
+    f32x16_t sc[Sh::kM];
+    scores(sc, Kt);
+    prep.template operator()<MASKED>(kb, sub, sc);
+    expv(kb, sub, sc, Vt);
+  };
+
   // Publish the prefetched tile, prefetch the next one, then every wave whose
   // row lists the block computes on it (the causal mask only in the row's
   // own diagonal block; the branches are wave-uniform).
   if constexpr (kDma) {
     // Wait for this wave's loads of tile `it`, then one barrier: every
     // wave's share has landed and every wave is done with the other stage,
-    // which then receives tile it+1 while tile it is used.
-    if (n_tiles > 0) dma_tile(0, tile_key0(0));
+    // which then receives tile it+1 while tile it is used (tile 0 is
+    // already on its way).
     for (int it = 0; it < n_tiles; ++it) {
       int kb;
       bool mine;
