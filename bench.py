@@ -319,7 +319,7 @@ def main(argv=None):
         "dense_tflops_exec": round(fc["dense_exec"] / (k2_ms * 1e-3) / 1e12, 2),
         "accum_tflops_exec": round(fc["dense_exec"] / (k1_ms * 1e-3) / 1e12, 2),
         "sparse_tflops_algorithmic": round(alg_tflops, 2),
-        "roofline": {"bound": "mfma", "kernel": "wise_attn_kernel<128,64,64,sparse>",
+        "roofline": {"bound": "mfma", "kernel": f"wise_attn_kernel (sparse, head_dim {D}, block {B})",
                      "achieved": round(alg_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(alg_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
