@@ -153,6 +153,7 @@ __host__ __device__ constexpr size_t attn_lds_need(int mode, int nblk) {
                                    DmaTile<D, KT, AttnShape<D, BLK, KT, RPW>::kThreads>::kStageBytes
                              : AttnShape<D, BLK, KT, RPW>::kTileLds) +
          (mode == kDenseMass ? (size_t)RPW * ((size_t)nblk * (BLK + 1) + BLK) * 4 : 0) +
+         (mode == kMassTwoPass ? (size_t)RPW * nblk * (BLK / 32) * 4 : 0) +
          (mode == kSparse ? (size_t)RPW * ((nblk + 31) / 32) * 4 + ((size_t)nblk + 1) * 4 : 0);
 }
 
@@ -293,6 +294,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
 
   float* part = reinterpret_cast<float*>(extra) + (size_t)slot * ((size_t)p.nblk * (BLK + 1) + BLK);
   float* invl = part + (size_t)p.nblk * (BLK + 1);                        // kDenseMass
+  float* slots = reinterpret_cast<float*>(extra);   // kMassTwoPass: [RPW][nblk][BLK/32]
 
   const size_t head_off = (size_t)bh * p.seq * D;
   const uint16_t* Qh = p.q + head_off;
@@ -345,11 +347,24 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
       dma16(vdesc, kbase + i * Dm::kWaves * 1024 + Dm::kTileBytes, dv[i], soff);
     }
   };
+  // K half only (first pass of the two-pass mass mode).
+  auto dma_k = [&](int stage, int key0) __attribute__((always_inline)) {
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)key0 * D * 2);
+    const uint32_t kbase = __builtin_amdgcn_readfirstlane(lds0 + stage * Dm::kStageBytes + wave_u * 1024);
+#pragma unroll
+    for (int i = 0; i < Dm::kInstr; ++i) dma16(kdesc, kbase + i * Dm::kWaves * 1024, dk[i], soff);
+  };
+
   // The first tile of every dense row and of every row the selection
   // writes is key block 0 (the sink), so its load is issued now, before the
   // list is known; the sparse prologue below re-issues it if the list
   // starts elsewhere.
-  if constexpr (kDma) dma_tile(0, 0);
+  if constexpr (MODE == kMassTwoPass) {
+    dma_k(0, 0);
+    for (int i = tid; i < RPW * p.nblk * WR; i += Sh::kThreads) slots[i] = 0.f;
+  } else if constexpr (kDma) {
+    dma_tile(0, 0);
+  }
 
   // Key blocks walked by the workgroup: the union of its rows' lists, in
   // ascending order, each entry tagged with the rows that list it.  Dense:
@@ -530,10 +545,113 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
     expv(kb, sub, sc, Vt);
   };
 
+  // Two-pass mass mode, first pass: running max and fp32 row sum only.
+  auto sum_tile = [&]<bool MASKED>(int kb, int sub, const uint16_t* Kt) __attribute__((always_inline)) {
+    f32x16_t sc[Sh::kM];
+    scores(sc, Kt);
+    prep.template operator()<MASKED>(kb, sub, sc);
+    const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
+    float tsum = 0.f;
+#pragma unroll
+    for (int m = 0; m < Sh::kM; ++m)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tsum += __builtin_amdgcn_exp2f(fmaf(sc[m][i], p.scale_log2, neg_m));
+    l_part += tsum;
+  };
+
+  // Two-pass mass mode, second pass: P = exp2(s*scale*log2e - m) / l with
+  // the final m and l of the first pass (fp32), summed into this wave's
+  // slot of the key block, and rounded to bf16 for O^T += V^T P^T.
+  auto mass_tile = [&]<bool MASKED>(int kb, int sub, const uint16_t* Kt, const uint16_t* Vt,
+                                    float neg_m, float inv_l) __attribute__((always_inline)) {
+    f32x16_t sc[Sh::kM];
+    scores(sc, Kt);
+    if constexpr (MASKED) {
+      const int rel = qrow - (kb * BLK + sub * KT);
+#pragma unroll
+      for (int m = 0; m < Sh::kM; ++m)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int koff = m * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+          sc[m][i] = (koff > rel) ? -INFINITY : sc[m][i];
+        }
+    }
+    float tsum = 0.f;
+#pragma unroll
+    for (int m = 0; m < Sh::kM; ++m) {
+      bf16x8_t pf[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sc[m][kk * 8 + e], p.scale_log2, neg_m)) * inv_l;
+          tsum += pv;
+          pf[kk][e] = (__bf16)pv;
+        }
+#pragma unroll
+      for (int t = 0; t < Sh::kDTiles; ++t)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const uint16_t* vp = Vt + voffs[t] + (32 * m + 16 * kk) * D;
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(vp));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(vp + 8 * D));
+          const bf16x8_t a =
+              __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], oacc[t], 0, 0, 0);
+        }
+    }
+    // sum over the wave's 32 queries x 2 key halves, fixed butterfly order
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) tsum += __shfl_xor(tsum, off);
+    if (lane == 0) slots[(slot * p.nblk + kb) * WR + wr] += tsum;
+  };
+
   // Publish the prefetched tile, prefetch the next one, then every wave whose
   // row lists the block computes on it (the causal mask only in the row's
   // own diagonal block; the branches are wave-uniform).
-  if constexpr (kDma) {
+  if constexpr (MODE == kMassTwoPass) {
+    // First pass: K tiles only; running max and row sum of every query.
+    for (int it = 0; it < n_tiles; ++it) {
+      int kb;
+      bool mine;
+      entry(it / Sh::kSub, kb, mine);
+      const int sub = it % Sh::kSub;
+      const int st = it & 1;
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      lds_barrier();
+      if (it + 1 < n_tiles) dma_k(st ^ 1, tile_key0(it + 1));
+      const uint16_t* Kt = reinterpret_cast<const uint16_t*>(smem + st * Dm::kStageBytes);
+      if (mine) {
+        if (kb == qb) sum_tile.template operator()<true>(kb, sub, Kt);
+        else sum_tile.template operator()<false>(kb, sub, Kt);
+      }
+    }
+    const float lt1 = l_part + __shfl_xor(l_part, 32);
+    const float inv_l = lt1 > 0.f ? 1.f / lt1 : 0.f;
+    const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
+    // Second pass over the same tiles with K and V.
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    lds_barrier();
+    dma_tile(0, tile_key0(0));
+    for (int it = 0; it < n_tiles; ++it) {
+      int kb;
+      bool mine;
+      entry(it / Sh::kSub, kb, mine);
+      const int sub = it % Sh::kSub;
+      const int st = it & 1;
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      lds_barrier();
+      if (it + 1 < n_tiles) dma_tile(st ^ 1, tile_key0(it + 1));
+      const uint16_t* Kt = reinterpret_cast<const uint16_t*>(smem + st * Dm::kStageBytes);
+      const uint16_t* Vt = Kt + KT * D;
+      if (mine) {
+        if (kb == qb) mass_tile.template operator()<true>(kb, sub, Kt, Vt, neg_m, inv_l);
+        else mass_tile.template operator()<false>(kb, sub, Kt, Vt, neg_m, inv_l);
+      }
+    }
+  } else if constexpr (kDma) {
     // Wait for this wave's loads of tile `it`, then one barrier: every
     // wave's share has landed and every wave is done with the other stage,
     // which then receives tile it+1 while tile it is used (tile 0 is
@@ -582,7 +700,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
 
   // ---- epilogue -----------------------------------------------------------
   const float lt = l_part + __shfl_xor(l_part, 32);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float inv = (MODE == kMassTwoPass) ? 1.f : (lt > 0.f ? 1.f / lt : 0.f);   // two-pass O is normalised
   if (row_ok) {
     uint16_t* Oh = p.o + head_off + (size_t)qrow * D;
 #pragma unroll
@@ -604,6 +722,19 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
     }
   }
 
+  if constexpr (MODE == kMassTwoPass) {
+    lds_barrier();
+    // r_qb = (1/B) * (sum of the row's wave slots, in wave order).
+    for (int w = tid; w < RPW * p.nblk; w += Sh::kThreads) {
+      const int r = w / p.nblk, b = w % p.nblk;
+      const int qr = q_lo + r;
+      if (qr >= p.nblk || b > qr) continue;
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < WR; ++i) acc += slots[(r * p.nblk + b) * WR + i];
+      p.mass[((size_t)bh * p.nblk + qr) * p.nblk + b] += acc * (1.0f / BLK);
+    }
+  }
   if constexpr (MODE == kDenseMass) {
     if (row_ok && g == 0) invl[wr * 32 + n] = inv;
     __syncthreads();
@@ -716,6 +847,33 @@ AttnCfg choose_cfg(int mode, int nblk) {
   return best;
 }
 
+#ifndef WISE_TWO_PASS_BELOW_WAVES
+#define WISE_TWO_PASS_BELOW_WAVES 4
+#endif
+
+// Resident waves per CU of the best single-pass mass configuration (0 if
+// none fits the LDS budget).
+template <int D, int BLK>
+int fused_mass_waves(int nblk) {
+  const AttnCfg c = choose_cfg<D, BLK>(kDenseMass, nblk);
+  if (c.kt == 0) return 0;
+  const size_t lds = cfg_lds<D, BLK>(c.kt, c.rpw, kDenseMass, nblk);
+  return std::min((int)(kMaxLds / lds) * (BLK / 32) * c.rpw, 8);
+}
+
+// The mass launch runs in one pass (O and the block mass from the same P,
+// with nB x (B+1) fp32 partials per row in LDS) unless those partials leave
+// fewer than WISE_TWO_PASS_BELOW_WAVES resident waves per CU; then it runs
+// in two passes over the keys (row max and sum, then normalised P), which
+// needs only one fp32 per (row, key block, wave) of LDS.
+template <int D, int BLK>
+int effective_mode(int mode, int nblk) {
+  if (mode != kDenseMass) return mode;
+  if (fused_mass_waves<D, BLK>(nblk) >= WISE_TWO_PASS_BELOW_WAVES) return kDenseMass;
+  const AttnCfg c = choose_cfg<D, BLK>(kMassTwoPass, nblk);
+  return c.kt != 0 ? kMassTwoPass : kDenseMass;
+}
+
 template <int D, int BLK, int MODE>
 hipError_t launch_cfg(AttnCfg c, const AttnParams& p, hipStream_t stream) {
   if constexpr (MODE != kDenseMass) {
@@ -741,23 +899,31 @@ hipError_t launch_cfg(AttnCfg c, const AttnParams& p, hipStream_t stream) {
 }
 
 template <int D, int BLK>
-hipError_t launch_attn_blk(int mode, const AttnParams& p, hipStream_t stream) {
+hipError_t launch_attn_blk(int mode_in, const AttnParams& p, hipStream_t stream) {
+  const int mode = effective_mode<D, BLK>(mode_in, p.nblk);
   const AttnCfg c = choose_cfg<D, BLK>(mode, p.nblk);
   if (c.kt == 0) return hipErrorInvalidValue;
   switch (mode) {
     case kDense: return launch_cfg<D, BLK, kDense>(c, p, stream);
     case kSparse: return launch_cfg<D, BLK, kSparse>(c, p, stream);
+    case kMassTwoPass: return launch_cfg<D, BLK, kMassTwoPass>(c, p, stream);
     default: return launch_cfg<D, BLK, kDenseMass>(c, p, stream);
   }
 }
 
+template <int D, int BLK>
+size_t attn_lds_bytes_blk(int mode_in, int nblk) {
+  const int mode = effective_mode<D, BLK>(mode_in, nblk);
+  const AttnCfg c = choose_cfg<D, BLK>(mode, nblk);
+  return c.kt ? cfg_lds<D, BLK>(c.kt, c.rpw, mode, nblk) : 0;
+}
+
 template <int D>
 size_t attn_lds_bytes_d(int block, int mode, int nblk) {
-  AttnCfg c{0, 0};
   switch (block) {
-    case 32: c = choose_cfg<D, 32>(mode, nblk); return c.kt ? cfg_lds<D, 32>(c.kt, c.rpw, mode, nblk) : 0;
-    case 64: c = choose_cfg<D, 64>(mode, nblk); return c.kt ? cfg_lds<D, 64>(c.kt, c.rpw, mode, nblk) : 0;
-    case 128: c = choose_cfg<D, 128>(mode, nblk); return c.kt ? cfg_lds<D, 128>(c.kt, c.rpw, mode, nblk) : 0;
+    case 32: return attn_lds_bytes_blk<D, 32>(mode, nblk);
+    case 64: return attn_lds_bytes_blk<D, 64>(mode, nblk);
+    case 128: return attn_lds_bytes_blk<D, 128>(mode, nblk);
   }
   return 0;
 }

@@ -7,11 +7,13 @@
 
 namespace wise {
 
-// Kinds of attention launch: the same kernel body serves all three.
+// Kinds of attention launch: the same kernel body serves all of them.
 enum AttnMode : int {
-  kDense = 0,      // Eq. (2) over every admissible key block
-  kDenseMass = 1,  // Eq. (2) plus the block mass of Eq. (5), added into `mass`
-  kSparse = 2      // Eq. (8): only the key blocks listed in the CSR row
+  kDense = 0,       // Eq. (2) over every admissible key block
+  kDenseMass = 1,   // Eq. (2) plus the block mass of Eq. (5), added into `mass`
+  kSparse = 2,      // Eq. (8): only the key blocks listed in the CSR row
+  kMassTwoPass = 3  // kDenseMass in two passes over the keys (launcher's choice
+                    // for long rows): row max and sum first, then normalised P
 };
 
 struct AttnParams {

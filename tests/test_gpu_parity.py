@@ -337,3 +337,45 @@ def test_small_trajectories_end_to_end():
         stats = _check(cfg, gm, rows, outs_h, samples, wl)
         say(f"  {stats['rows']} rows, margin rows {stats['margin_rows']}, "
             f"max-abs {stats['max_abs']:.2e}, mean-abs {np.mean(stats['mean_abs']):.2e}")
+
+
+# Long rows: the mass launch switches to its two-pass form (row max and sum
+# first, then normalised probabilities) when one-pass LDS partials would
+# leave too few resident waves.  (batch, heads, seq, head_dim, block)
+LONG_SHAPES = [
+    (1, 1, 32768, 128, 64),
+    (1, 2, 8192, 64, 32),
+    (1, 1, 40960, 96, 128),
+]
+
+
+@pytest.mark.parametrize("shape", LONG_SHAPES, ids=[f"b{s[0]}h{s[1]}s{s[2]}d{s[3]}B{s[4]}" for s in LONG_SHAPES])
+def test_accum_long_rows_matches_oracle(shape):
+    b_, h_, s_, d_, blk = shape
+    say(f"accum long rows {shape}")
+    steps = _steps(_cfg(*shape), 2)
+    nb = s_ // blk
+    mass = torch.zeros(b_, h_, nb, nb, dtype=torch.float32, device="cuda")
+    qbs = sorted({0, 1, nb // 3, nb - 2, nb - 1})
+    outs = []
+    for _, q, k, v in steps:
+        o = wise.wise_full_attn_accum(to_dev(q), to_dev(k), to_dev(v), mass, blk)
+        outs.append({qb: bf16_dev_to_f64(o[:, :, qb * blk:(qb + 1) * blk]) for qb in qbs})
+    torch.cuda.synchronize()
+    mass_h = mass.cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(mass_h.sum(axis=-1), 2.0, atol=1e-4)
+    iu = np.triu_indices(nb, 1)
+    assert np.all(mass_h[..., iu[0], iu[1]] == 0.0)
+    sc = oracle.default_scale(d_)
+    for b in range(b_):
+        for h in range(h_):
+            ref = np.zeros((len(qbs), nb))
+            for t, (_, q, k, v) in enumerate(steps):
+                Q, K, V = (_oracle_head(x, b, h) for x in (q, k, v))
+                ref += oracle.block_mass(Q, K, sc, blk, qblocks=qbs)
+                for qb in qbs:
+                    rows = np.arange(qb * blk, (qb + 1) * blk)
+                    compare_outputs(outs[t][qb][b, h], oracle.dense_attention(Q, K, V, sc, rows),
+                                    f"O t{t} b{b}h{h}q{qb}")
+            err = np.abs(mass_h[b, h][qbs] - ref)
+            assert err.max() <= mass_tolerance(2), err.max()
