@@ -509,6 +509,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
             tsum = __builtin_amdgcn_fdot2_f32_bf16(pair, one, tsum, false);
           }
       }
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int t = 0; t < Sh::kDTiles; ++t)
 #pragma unroll
@@ -525,6 +526,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
           oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], oacc[t], 0, 0, 0);
         }
     }
+    __builtin_amdgcn_s_setprio(0);
     l_part += tsum;
     if constexpr (MODE == kDenseMass) {
       blk_part += tsum;
@@ -537,10 +539,15 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   };
 
   // One whole tile for this wave's row.
+  // The MFMA stretches run at raised wave priority: when both waves of a
+  // SIMD are ready, the one feeding the matrix core issues first and the
+  // other's softmax work fills the MFMA shadow.
   auto compute_tile = [&]<bool MASKED>(int kb, int sub, const uint16_t* Kt,
                                        const uint16_t* Vt) __attribute__((always_inline)) {
     f32x16_t sc[Sh::kM];
+    __builtin_amdgcn_s_setprio(1);
     scores(sc, Kt);
+    __builtin_amdgcn_s_setprio(0);
     prep.template operator()<MASKED>(kb, sub, sc);
     expv(kb, sub, sc, Vt);
   };
