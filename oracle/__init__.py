@@ -36,6 +36,14 @@ with their reasons in the design notes):
    diagonal block's mass counts only admissible keys j <= i.
 6. If rounding leaves the total admissible mass below eta, every admissible
    block is kept.
+7. Selection variants (Eq. (6) left / Eq. (18) temporal union; Appendix B
+   controls Eq. (19)-(22)) take single-step block masses r^(t) and work on the
+   eta-ranked part only; the sink and diagonal blocks are added to every
+   variant's result afterwards, as for the main selection.  The union is over
+   the steps passed in (the paper's window is the last four discovery steps);
+   "the first recurrent step" of the controls is the first discovery step
+   (0-based step 0).  m_q^WISE and K_q of Eq. (20) and (22) are taken over the
+   union's eta-ranked part, and m_q^WISE is summed in float64.
 
 Inputs are float64 arrays (``bf16_to_f64`` widens bf16 bits exactly).
 """
@@ -50,6 +58,8 @@ __all__ = [
     "bf16_to_f64", "default_scale", "attention_weights", "attention_output",
     "dense_attention", "block_mass", "block_mass_rows", "mean_block_mass",
     "select_support", "support_margins", "working_set_mask",
+    "eta_support", "topk_support", "select_union", "select_static",
+    "select_mass_matched", "select_size_matched",
     "masked_attention_weights", "masked_attention", "trajectory_head",
 ]
 
@@ -142,6 +152,30 @@ def _ranked(mbar_row, q: int) -> List[int]:
     return sorted(range(q + 1), key=lambda b: (-float(mbar_row[b]), b))
 
 
+def eta_support(mass_row, q: int, eta: float) -> List[int]:
+    """The cumulative-eta block support of Eq. (6) (right-hand part) and
+    Eq. (12): the k* highest-mass admissible blocks of query block q, where
+    k* is the smallest k whose k largest masses sum to at least eta (reading
+    3: inclusive; reading 6: all blocks if eta is never reached).  Ranked
+    part only, ascending ids.  The same set is the B_q^(t,rho) of the
+    controls in Appendix B."""
+    order = _ranked(mass_row, q)
+    prefix = 0.0
+    k_star = len(order)
+    for k, b in enumerate(order, start=1):
+        prefix += float(mass_row[b])
+        if prefix >= eta:
+            k_star = k
+            break
+    return sorted(order[:k_star])
+
+
+def topk_support(mass_row, q: int, k: int) -> List[int]:
+    """TopK of Eq. (22): the k highest-mass admissible blocks (ties to the
+    lower index, reading 2), ascending ids."""
+    return sorted(_ranked(mass_row, q)[:max(0, k)])
+
+
 def select_support(mbar_row, q: int, eta: float, cap: int = 0) -> List[int]:
     """Working set of query block q, ascending block ids.
 
@@ -149,17 +183,49 @@ def select_support(mbar_row, q: int, eta: float, cap: int = 0) -> List[int]:
     least eta; the top-k* blocks (capped at ``cap`` when cap > 0) are taken,
     then the sink block 0 and the diagonal block q are added (reading 4).
     """
-    order = _ranked(mbar_row, q)
-    prefix = 0.0
-    k_star = len(order)                  # reading 6: keep all if eta is never reached
-    for k, b in enumerate(order, start=1):
-        prefix += float(mbar_row[b])
-        if prefix >= eta:                # reading 3: inclusive
-            k_star = k
-            break
-    k = min(k_star, cap) if cap > 0 else k_star
-    chosen = set(order[:k]) | {0, q}
-    return sorted(chosen)
+    ranked = eta_support(mbar_row, q, eta)
+    if cap > 0 and len(ranked) > cap:
+        ranked = topk_support(mbar_row, q, cap)   # the cap keeps the top `cap` of the same order
+    return sorted(set(ranked) | {0, q})
+
+
+def _union_ranked(step_rows, q: int, eta: float) -> List[int]:
+    out = set()
+    for r in step_rows:
+        out |= set(eta_support(r, q, eta))
+    return sorted(out)
+
+
+def select_union(step_rows, q: int, eta: float) -> List[int]:
+    """WISE working set with temporal union, Eq. (6) (left) / Eq. (18):
+    the union over the given discovery steps of each step's own eta-support
+    of r^(t), plus sink and diagonal (reading 7)."""
+    return sorted(set(_union_ranked(step_rows, q, eta)) | {0, q})
+
+
+def select_static(first_row, q: int, eta: float) -> List[int]:
+    """Static-95 control, Eq. (19): the eta-support of the first step's block
+    masses (eta = 0.95 in the paper), plus sink and diagonal."""
+    return sorted(set(eta_support(first_row, q, eta)) | {0, q})
+
+
+def select_mass_matched(first_row, window_rows, q: int, eta: float) -> List[int]:
+    """MassMatched control, Eq. (20)-(21): m = the first step's mass covered
+    by the union working set W_q (Eq. 20, float64 sum in block order), then
+    the smallest first-step-ranked prefix whose mass reaches m; plus sink and
+    diagonal."""
+    w = _union_ranked(window_rows, q, eta)
+    m = 0.0
+    for b in w:
+        m += float(first_row[b])
+    return sorted(set(eta_support(first_row, q, m)) | {0, q})
+
+
+def select_size_matched(first_row, window_rows, q: int, eta: float) -> List[int]:
+    """SizeMatched control, Eq. (22): the K_q = |W_q| highest first-step
+    masses, plus sink and diagonal."""
+    k = len(_union_ranked(window_rows, q, eta))
+    return sorted(set(topk_support(first_row, q, k)) | {0, q})
 
 
 def support_margins(mbar_row, q: int, eta: float) -> Dict[str, float]:

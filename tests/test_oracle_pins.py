@@ -28,7 +28,12 @@ def _impl(**over):
     ns = SimpleNamespace(attention_weights=oracle.attention_weights,
                          block_mass_rows=oracle.block_mass_rows,
                          select_support=oracle.select_support,
-                         masked_attention_weights=oracle.masked_attention_weights)
+                         masked_attention_weights=oracle.masked_attention_weights,
+                         eta_support=oracle.eta_support,
+                         select_union=oracle.select_union,
+                         select_static=oracle.select_static,
+                         select_mass_matched=oracle.select_mass_matched,
+                         select_size_matched=oracle.select_size_matched)
     for k, v in over.items():
         setattr(ns, k, v)
     return ns
@@ -304,6 +309,76 @@ def pin_masked_rows_normalised(impl):
         assert np.all(a[i, ~allowed] == 0) and np.all(a[i, allowed] > 0)
 
 
+def pin_variants_golden(impl):
+    """Hand-worked dyadic cases of Eq. (6)/(18), (19), (20)-(21), (22)."""
+    with open(os.path.join(GOLDEN, "selection_variants_dyadic.json")) as f:
+        g = json.load(f)
+    for case in g["cases"]:
+        q, eta = case["q"], case["eta"]
+        first = np.array(case["first"])
+        window = [np.array(w) for w in case["window"]]
+        assert impl.eta_support(first, q, eta) == case["first_support"], case["note"]
+        assert [impl.eta_support(w, q, eta) for w in window] == case["window_supports"], case["note"]
+        assert impl.select_union(window, q, eta) == case["union"], case["note"]
+        assert impl.select_static(first, q, eta) == case["static"], case["note"]
+        assert impl.select_mass_matched(first, window, q, eta) == case["mass_matched"], case["note"]
+        assert impl.select_size_matched(first, window, q, eta) == case["size_matched"], case["note"]
+
+
+def pin_eta_support_brute_force(impl):
+    """Eq. (6) right: the per-step support is a minimum-cardinality set
+    reaching eta and consists of the highest masses (distinct masses)."""
+    g = np.random.default_rng(21)
+    for trial in range(60):
+        q = int(g.integers(0, 10))
+        r = g.dirichlet(np.full(q + 1, 0.5))
+        eta = float(g.choice([0.5, 0.8, 0.95]))
+        got = impl.eta_support(r, q, eta)
+        size, feasible = _brute_force_support(r, q, eta)
+        assert len(got) == size, (trial, got, size)
+        assert tuple(got) in [tuple(sorted(c)) for c in feasible]
+        assert min(r[got]) >= max([r[b] for b in range(q + 1) if b not in got], default=-1.0)
+
+
+def pin_union_structure(impl):
+    """Eq. (18): the union contains every step's own support and nothing
+    else (besides sink/diagonal); one step gives that step's support; equal
+    steps give the single-step selection."""
+    g = np.random.default_rng(22)
+    for trial in range(40):
+        q = int(g.integers(1, 30))
+        steps = [g.dirichlet(np.full(q + 1, 0.4)) for _ in range(int(g.integers(1, 5)))]
+        eta = float(g.choice([0.6, 0.9, 0.95]))
+        got = set(impl.select_union(steps, q, eta))
+        parts = [set(impl.eta_support(r, q, eta)) for r in steps]
+        assert got == set().union(*parts) | {0, q}, trial
+        assert impl.select_union(steps[:1], q, eta) == sorted(parts[0] | {0, q})
+        assert impl.select_union([steps[0]] * 3, q, eta) == impl.select_support(steps[0], q, eta)
+        assert impl.select_static(steps[0], q, eta) == impl.select_support(steps[0], q, eta)
+
+
+def pin_matched_controls(impl):
+    """Eq. (20)-(22) on random rows: MassMatched is the shortest first-step
+    prefix reaching the union's first-step mass; SizeMatched keeps exactly
+    |union| first-step-ranked blocks."""
+    g = np.random.default_rng(23)
+    for trial in range(60):
+        q = int(g.integers(2, 40))
+        first = g.dirichlet(np.full(q + 1, 0.5))
+        window = [g.dirichlet(np.full(q + 1, 0.3)) for _ in range(4)]
+        eta = float(g.choice([0.7, 0.9, 0.95]))
+        union = set().union(*[set(impl.eta_support(r, q, eta)) for r in window])
+        order = sorted(range(q + 1), key=lambda b: (-first[b], b))
+        m = sum(first[b] for b in sorted(union))
+        mm = impl.select_mass_matched(first, window, q, eta)
+        k = 1
+        while sum(first[b] for b in order[:k]) < m and k <= q:
+            k += 1
+        assert mm == sorted(set(order[:k]) | {0, q}), (trial, mm, k)
+        sm = impl.select_size_matched(first, window, q, eta)
+        assert sm == sorted(set(order[:len(union)]) | {0, q}), (trial, sm)
+
+
 PINS = [pin_uniform_when_q_zero, pin_constant_values, pin_single_position,
         pin_logistic_two_keys, pin_causal_rows_sum_to_one, pin_key_shift_invariance,
         pin_scale_is_a_temperature, pin_golden_dense, pin_block_mass_sums_to_one,
@@ -312,7 +387,9 @@ PINS = [pin_uniform_when_q_zero, pin_constant_values, pin_single_position,
         pin_selection_eta_one_keeps_all, pin_selection_small_eta_keeps_argmax,
         pin_selection_golden, pin_selection_perturbation,
         pin_full_support_reproduces_dense, pin_diagonal_only_support,
-        pin_sink_and_diagonal_support, pin_masked_rows_normalised]
+        pin_sink_and_diagonal_support, pin_masked_rows_normalised,
+        pin_variants_golden, pin_eta_support_brute_force, pin_union_structure,
+        pin_matched_controls]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -467,7 +544,53 @@ def _mut_masked_ignores_support(q, k, scale, block, supports, rows):
     return oracle.masked_attention_weights(q, k, scale, block, full, rows)
 
 
+def _mut_union_is_intersection(steps, q, eta):
+    parts = [set(oracle.eta_support(r, q, eta)) for r in steps]
+    return sorted(set.intersection(*parts) | {0, q})
+
+
+def _mut_union_of_mean(steps, q, eta):
+    return oracle.select_support(oracle.mean_block_mass(steps), q, eta)
+
+
+def _mut_static_uses_last_step(first, q, eta):
+    return oracle.select_static(np.roll(first, 1), q, eta)
+
+
+def _mut_mass_matched_counts_sink(first, window, q, eta):
+    w = set(oracle.select_union(window, q, eta))        # includes sink and diagonal
+    m = sum(float(first[b]) for b in sorted(w))
+    return sorted(set(oracle.eta_support(first, q, m)) | {0, q})
+
+
+def _mut_mass_matched_uses_window_ranking(first, window, q, eta):
+    return oracle.select_mass_matched(window[0], window, q, eta)
+
+
+def _mut_size_matched_one_more(first, window, q, eta):
+    k = len(oracle.select_union(window, q, eta)) - 1    # sink/diagonal counted, minus one
+    return sorted(set(oracle.topk_support(first, q, k)) | {0, q})
+
+
+def _mut_eta_support_exclusive(r, q, eta):
+    order = sorted(range(q + 1), key=lambda b: (-float(r[b]), b))
+    prefix, k_star = 0.0, q + 1
+    for kk, b in enumerate(order, 1):
+        prefix += float(r[b])
+        if prefix > eta:
+            k_star = kk
+            break
+    return sorted(order[:k_star])
+
+
 MUTANTS = {
+    "union_is_intersection": dict(select_union=_mut_union_is_intersection),
+    "union_selects_on_mean": dict(select_union=_mut_union_of_mean),
+    "static_wrong_step": dict(select_static=_mut_static_uses_last_step),
+    "mass_matched_counts_sink": dict(select_mass_matched=_mut_mass_matched_counts_sink),
+    "mass_matched_wrong_ranking": dict(select_mass_matched=_mut_mass_matched_uses_window_ranking),
+    "size_matched_off_by_one": dict(select_size_matched=_mut_size_matched_one_more),
+    "eta_support_exclusive": dict(eta_support=_mut_eta_support_exclusive),
     "transposed_operand": dict(attention_weights=_mut_transposed),
     "missing_scale": dict(attention_weights=_mut_no_scale),
     "causal_off_by_one": dict(attention_weights=_mut_mask_off_by_one),
