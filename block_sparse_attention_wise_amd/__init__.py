@@ -20,7 +20,8 @@ import os
 from typing import Optional, Tuple
 
 __all__ = ["WiseError", "WiseDesc", "load_library", "library_path", "wise_full_attn",
-           "wise_full_attn_accum", "wise_select_support", "wise_sparse_attn",
+           "wise_full_attn_accum", "wise_select_support", "wise_select_variant", "wise_sparse_attn",
+           "SELECT_UNION", "SELECT_STATIC", "SELECT_MASS_MATCHED", "SELECT_SIZE_MATCHED",
            "wise_select_max_nnz", "wise_abi_version", "WISE_OK", "WISE_ERR_INVALID_ARG",
            "WISE_ERR_UNSUPPORTED", "WISE_ERR_CAPACITY", "WISE_ERR_HIP"]
 
@@ -68,6 +69,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "wise_full_attn": ([dp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "wise_full_attn_accum": ([dp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "wise_select_support": ([dp, vp, i32, ctypes.c_double, i32, vp, vp, i64, vp], ctypes.c_int),
+        "wise_select_variant": ([dp, i32, vp, i32, ctypes.c_double, vp, vp, i64, vp], ctypes.c_int),
         "wise_sparse_attn": ([dp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "wise_select_max_nnz": ([dp, i32], i64),
         "wise_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -223,6 +225,38 @@ def wise_select_support(mass, n_steps: int, eta: float, head_dim: int, block_siz
                                             col_idx.data_ptr(), col_idx.numel(),
                                             _stream_ptr(stream))
     _check(st, "wise_select_support")
+    return row_ptr, col_idx
+
+
+SELECT_UNION, SELECT_STATIC, SELECT_MASS_MATCHED, SELECT_SIZE_MATCHED = 1, 2, 3, 4
+
+
+def wise_select_variant(kind: int, step_mass, eta: float, head_dim: int, block_size: int,
+                        row_ptr=None, col_idx=None, stream=None) -> Tuple[object, object]:
+    """Selection variants (temporal union, Static, MassMatched, SizeMatched)
+    over single-step masses ``step_mass`` [n_mass, batch, heads, nB, nB]
+    -> (row_ptr, col_idx) CSR."""
+    torch = _torch()
+    _need(step_mass, "step_mass", torch.float32, 5)
+    n_mass, b, h, nb, nb2 = step_mass.shape
+    if nb != nb2:
+        raise ValueError("step_mass must be [n_mass, batch, heads, n_blocks, n_blocks]")
+    seq = nb * block_size
+    d = WiseDesc(b, h, seq, head_dim, block_size, 0.0)
+    cap = wise_select_max_nnz(b, h, seq, head_dim, block_size, 0)
+    n_rows = b * h * nb
+    if row_ptr is None:
+        row_ptr = torch.empty(n_rows + 1, dtype=torch.int32, device=step_mass.device)
+    if col_idx is None:
+        col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=step_mass.device)
+    _need(row_ptr, "row_ptr", torch.int32, 1)
+    _need(col_idx, "col_idx", torch.int32, 1)
+    if row_ptr.numel() != n_rows + 1:
+        raise ValueError(f"row_ptr must have {n_rows + 1} entries")
+    st = load_library().wise_select_variant(ctypes.byref(d), int(kind), step_mass.data_ptr(), int(n_mass),
+                                            float(eta), row_ptr.data_ptr(), col_idx.data_ptr(),
+                                            col_idx.numel(), _stream_ptr(stream))
+    _check(st, "wise_select_variant")
     return row_ptr, col_idx
 
 

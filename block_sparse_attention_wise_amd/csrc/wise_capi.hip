@@ -206,6 +206,48 @@ wise_status_t wise_select_support(const wise_attn_desc_t* desc, const float* mas
   return ok();
 }
 
+wise_status_t wise_select_variant(const wise_attn_desc_t* desc, int32_t kind, const float* step_mass,
+                                  int32_t n_mass, double eta, int32_t* row_ptr, int32_t* col_idx,
+                                  int64_t col_capacity, void* stream) {
+  int32_t nblk;
+  int64_t n_rows;
+  wise_status_t st = check_desc(desc, &nblk, &n_rows);
+  if (st != WISE_OK) return st;
+  if (step_mass == nullptr || row_ptr == nullptr || col_idx == nullptr)
+    return fail(WISE_ERR_INVALID_ARG, "step_mass / row_ptr / col_idx is NULL");
+  if ((reinterpret_cast<uintptr_t>(step_mass) | reinterpret_cast<uintptr_t>(row_ptr) |
+       reinterpret_cast<uintptr_t>(col_idx)) & 3u)
+    return fail(WISE_ERR_INVALID_ARG, "step_mass / row_ptr / col_idx not 4-byte aligned");
+  if (kind < WISE_SELECT_UNION || kind > WISE_SELECT_SIZE_MATCHED)
+    return fail(WISE_ERR_INVALID_ARG, "unknown selection kind %d", kind);
+  const int32_t min_mass = (kind == WISE_SELECT_UNION || kind == WISE_SELECT_STATIC) ? 1 : 2;
+  if (n_mass < min_mass || (kind == WISE_SELECT_STATIC && n_mass != 1))
+    return fail(WISE_ERR_INVALID_ARG, "n_mass %d invalid for selection kind %d", n_mass, kind);
+  if (!(eta > 0.0 && eta <= 1.0)) return fail(WISE_ERR_INVALID_ARG, "eta %g outside (0, 1]", eta);
+  if (nblk > 64 * 32) return fail(WISE_ERR_UNSUPPORTED, "n_blocks %d above 2048", nblk);
+  const int64_t need = max_nnz(nblk, (int64_t)desc->batch * desc->heads, 0);
+  if (need >= (int64_t)INT32_MAX)
+    return fail(WISE_ERR_UNSUPPORTED, "worst-case nnz %lld does not fit int32", (long long)need);
+  if (col_capacity < need)
+    return fail(WISE_ERR_CAPACITY, "col_capacity %lld below worst-case nnz %lld", (long long)col_capacity,
+                (long long)need);
+  SelectParams p{};
+  p.mass = step_mass;
+  p.row_ptr = row_ptr;
+  p.col_idx = col_idx;
+  p.n_rows = (int32_t)n_rows;
+  p.nblk = nblk;
+  p.max_blocks = 0;
+  p.n_steps = 1.0;
+  p.eta = eta;
+  p.kind = kind;
+  p.n_mass = n_mass;
+  p.mass_stride = n_rows * nblk;
+  const hipError_t e = launch_select(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(WISE_ERR_HIP, "selection launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* wise_status_string(wise_status_t status) {
   switch (status) {
     case WISE_OK: return "WISE_OK";

@@ -49,15 +49,27 @@ hipError_t launch_attn_d64(int block, int mode, const AttnParams& p, hipStream_t
 hipError_t launch_attn_d96(int block, int mode, const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_d128(int block, int mode, const AttnParams& p, hipStream_t stream);
 
+// Selection kinds (values match wise_select_kind_t, 0 = the main selection).
+enum SelectKind : int {
+  kSelMean = 0,         // Eq. (6) on the mean of the accumulated discovery masses
+  kSelUnion = 1,        // Eq. (6) left / Eq. (18): union of per-step supports
+  kSelStatic = 2,       // Eq. (19): first step's support
+  kSelMassMatched = 3,  // Eq. (20)-(21)
+  kSelSizeMatched = 4   // Eq. (22)
+};
+
 struct SelectParams {
-  const float* mass;
+  const float* mass;   // kSelMean: accumulated sum; else [n_mass] single-step masses
   int32_t* row_ptr;
   int32_t* col_idx;
   int32_t n_rows;
   int32_t nblk;
-  int32_t max_blocks;  // 0 = no cap
-  double n_steps;      // discovery steps summed into mass
+  int32_t max_blocks;  // 0 = no cap (kSelMean only)
+  double n_steps;      // discovery steps summed into mass (kSelMean)
   double eta;
+  int32_t kind;        // SelectKind
+  int32_t n_mass;      // step masses given (variants)
+  int64_t mass_stride; // elements between consecutive step masses
 };
 
 hipError_t launch_select(const SelectParams& p, hipStream_t stream);

@@ -14,6 +14,12 @@
 // applied the same way with counts instead of masses.  Ballots give index
 // order and the compacted, ascending CSR output.
 //
+// Variants (same machinery): the temporal union of per-step supports
+// (Eq. 6 left / Eq. 18), and the controls of Appendix B: Static-95 (Eq. 19),
+// MassMatched (Eq. 20-21: the first step's mass covered by the union becomes
+// the threshold of the first step's own ranking) and SizeMatched (Eq. 22:
+// the union's size becomes a top-k count on the first step).
+//
 // Three launches build the CSR without scratch memory: count (row lengths
 // into row_ptr[1..]), an in-place scan of row_ptr, and fill (the same
 // deterministic selection again, written at row_ptr[row]).
@@ -41,102 +47,150 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask, int lane) {
   return (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
 }
 
+// One row's masses as held by a wavefront: element e = 64*j + lane in slot
+// j; fp32 bit patterns (non-negative, so they order like the values) and
+// the float64 values the sums use.
+template <int EPL>
+struct RowMass {
+  uint32_t bits[EPL];
+  double val[EPL];
+  uint32_t valid;  // bit j: element 64*j + lane is admissible (e <= q)
+  double div;      // val = fp32 value / div
+};
+
+template <int EPL>
+__device__ __forceinline__ RowMass<EPL> load_row(const float* mrow, int n, double div, int lane) {
+  RowMass<EPL> r;
+  r.valid = 0;
+  r.div = div;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = 64 * j + lane;
+    const bool v = e < n;
+    const float x = v ? mrow[e] : 0.f;
+    r.bits[j] = __float_as_uint(x);
+    r.val[j] = v ? (double)x / div : 0.0;
+    if (v) r.valid |= 1u << j;
+  }
+  return r;
+}
+
+template <int EPL>
+__device__ __forceinline__ double mass_at_least(const RowMass<EPL>& r, uint32_t t) {
+  double s = 0.0;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j)
+    if (((r.valid >> j) & 1u) && r.bits[j] >= t) s += r.val[j];
+  return wave_sum(s);
+}
+
+template <int EPL>
+__device__ __forceinline__ int count_at_least(const RowMass<EPL>& r, uint32_t t) {
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j)
+    if (((r.valid >> j) & 1u) && r.bits[j] >= t) ++c;
+  return wave_isum(c);
+}
+
+// Keep-set {bits > t} plus the first `ties` elements (index order) with
+// bits == t.
+template <int EPL>
+__device__ __forceinline__ uint32_t keep_flags(const RowMass<EPL>& r, uint32_t t, int ties, int lane) {
+  uint32_t f = 0;
+  int seen = 0;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const bool v = (r.valid >> j) & 1u;
+    const bool tie = v && r.bits[j] == t;
+    const uint64_t tb = __ballot(tie);
+    const int rank = seen + (int)lanes_below(tb, lane);
+    if (v && (r.bits[j] > t || (tie && rank < ties))) f |= 1u << j;
+    seen += (int)__popcll(tb);
+  }
+  return f;
+}
+
+// The cumulative-eta support (Eq. 6 right / Eq. 12): the smallest set of
+// highest-mass admissible blocks (ties to the lower index) whose float64
+// mass reaches eta; every admissible block when the total stays below eta.
+template <int EPL>
+__device__ uint32_t eta_flags(const RowMass<EPL>& r, double eta, int lane) {
+  if (mass_at_least(r, 0u) < eta) return r.valid;
+  uint32_t t = 0;
+  for (int bit = 30; bit >= 0; --bit) {
+    const uint32_t cand = t | (1u << bit);
+    if (mass_at_least(r, cand) >= eta) t = cand;
+  }
+  // Mass strictly above t*, then ties in index order until eta is reached
+  // (t* has bit 31 clear, so t* + 1 does not wrap).
+  const double above = mass_at_least(r, t + 1u);
+  const double tie_val = (double)__uint_as_float(t) / r.div;   // the value of every tied element
+  int need = 0;
+  double pref = above;
+  bool done = false;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    uint64_t tb = __ballot(((r.valid >> j) & 1u) && r.bits[j] == t);
+    while (tb != 0 && !done) {  // wave-uniform
+      tb &= tb - 1;
+      pref += tie_val;
+      ++need;
+      if (pref >= eta) done = true;
+    }
+  }
+  return keep_flags(r, t, need, lane);
+}
+
+// The k highest-mass admissible blocks (ties to the lower index): largest
+// t with at least k blocks >= t, then ties at t in index order.
+template <int EPL>
+__device__ uint32_t topk_flags(const RowMass<EPL>& r, int k, int lane) {
+  uint32_t t = 0;
+  for (int bit = 30; bit >= 0; --bit) {
+    const uint32_t cand = t | (1u << bit);
+    if (count_at_least(r, cand) >= k) t = cand;
+  }
+  return keep_flags(r, t, k - count_at_least(r, t + 1u), lane);
+}
+
+template <int EPL>
+__device__ __forceinline__ int flag_count(uint32_t f) {
+  return wave_isum(__popc(f));
+}
+
 // Selection flags of one row; bit j of the result is set when element
 // e = 64*j + lane is kept.  EPL = elements per lane (n_blocks <= 64*EPL).
 template <int EPL>
 __device__ uint32_t select_row(const SelectParams& p, int row, int lane) {
   const int q = row % p.nblk;
   const int n = q + 1;
-  const float* mrow = p.mass + (size_t)row * p.nblk;
+  auto step_row = [&](int w) { return p.mass + (size_t)w * p.mass_stride + (size_t)row * p.nblk; };
 
-  uint32_t bits[EPL];
-  double mbar[EPL];
-  uint32_t valid = 0;
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) {
-    const int e = 64 * j + lane;
-    const bool v = e < n;
-    const float x = v ? mrow[e] : 0.f;
-    bits[j] = __float_as_uint(x);
-    mbar[j] = v ? (double)x / p.n_steps : 0.0;
-    if (v) valid |= 1u << j;
-  }
-
-  auto mass_at_least = [&](uint32_t t) {
-    double s = 0.0;
-#pragma unroll
-    for (int j = 0; j < EPL; ++j)
-      if (((valid >> j) & 1u) && bits[j] >= t) s += mbar[j];
-    return wave_sum(s);
-  };
-  auto count_at_least = [&](uint32_t t) {
-    int c = 0;
-#pragma unroll
-    for (int j = 0; j < EPL; ++j)
-      if (((valid >> j) & 1u) && bits[j] >= t) ++c;
-    return wave_isum(c);
-  };
-  // Keep-set {bits > t} plus the first `ties` elements (index order) with
-  // bits == t.  ties < 0 means all of them.
-  auto keep_flags = [&](uint32_t t, int ties) {
-    uint32_t f = 0;
-    int seen = 0;
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      const bool v = (valid >> j) & 1u;
-      const bool tie = v && bits[j] == t;
-      const uint64_t tb = __ballot(tie);
-      const int rank = seen + (int)lanes_below(tb, lane);
-      if (v && (bits[j] > t || (tie && (ties < 0 || rank < ties)))) f |= 1u << j;
-      seen += (int)__popcll(tb);
-    }
-    return f;
-  };
-
-  uint32_t flags;
-  int k_star;
-  if (mass_at_least(0u) < p.eta) {
-    // Rounding left the total below eta: every admissible block is kept.
-    flags = valid;
-    k_star = n;
+  uint32_t flags = 0;
+  if (p.kind == kSelMean) {
+    const RowMass<EPL> r = load_row<EPL>(step_row(0), n, p.n_steps, lane);
+    flags = eta_flags(r, p.eta, lane);
+    if (p.max_blocks > 0 && flag_count<EPL>(flags) > p.max_blocks) flags = topk_flags(r, p.max_blocks, lane);
+  } else if (p.kind == kSelUnion || p.kind == kSelStatic) {
+    // Eq. (6) left / Eq. (18): union of every given step's own eta-support
+    // (Static-95, Eq. 19: the single first step).
+    for (int w = 0; w < p.n_mass; ++w) flags |= eta_flags(load_row<EPL>(step_row(w), n, 1.0, lane), p.eta, lane);
   } else {
-    uint32_t t = 0;
-    for (int bit = 30; bit >= 0; --bit) {
-      const uint32_t cand = t | (1u << bit);
-      if (mass_at_least(cand) >= p.eta) t = cand;
-    }
-    // Mass strictly above t*, then ties in index order until eta is reached
-    // (t* has bit 31 clear, so t* + 1 does not wrap).
-    const double above = mass_at_least(t + 1u);
-    const int n_above = count_at_least(t + 1u);
-    const double tie_val = (double)__uint_as_float(t) / p.n_steps;
-    int need = 0;
-    double pref = above;
-    bool done = false;
+    // Controls of Eq. (20)-(22): the union W of steps 1..n_mass-1, then the
+    // first step's own ranking (step 0).
+    uint32_t u = 0;
+    for (int w = 1; w < p.n_mass; ++w) u |= eta_flags(load_row<EPL>(step_row(w), n, 1.0, lane), p.eta, lane);
+    const RowMass<EPL> a = load_row<EPL>(step_row(0), n, 1.0, lane);
+    if (p.kind == kSelMassMatched) {
+      double m = 0.0;
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      uint64_t tb = __ballot(((valid >> j) & 1u) && bits[j] == t);
-      while (tb != 0 && !done) {  // wave-uniform
-        tb &= tb - 1;
-        pref += tie_val;
-        ++need;
-        if (pref >= p.eta) done = true;
-      }
+      for (int j = 0; j < EPL; ++j)
+        if ((u >> j) & 1u) m += a.val[j];
+      flags = eta_flags(a, wave_sum(m), lane);
+    } else {
+      flags = topk_flags(a, flag_count<EPL>(u), lane);
     }
-    flags = keep_flags(t, need);
-    k_star = n_above + need;
-  }
-
-  if (p.max_blocks > 0 && k_star > p.max_blocks) {
-    // Top max_blocks by (mass desc, index asc): largest t2 with at least
-    // max_blocks blocks >= t2, then ties at t2 in index order.
-    uint32_t t2 = 0;
-    for (int bit = 30; bit >= 0; --bit) {
-      const uint32_t cand = t2 | (1u << bit);
-      if (count_at_least(cand) >= p.max_blocks) t2 = cand;
-    }
-    const int n_above = count_at_least(t2 + 1u);
-    flags = keep_flags(t2, p.max_blocks - n_above);
   }
 
   // Sink and diagonal blocks are always kept.

@@ -11,6 +11,7 @@
  *   wise_full_attn        dense causal attention (Section 3, Eq. 2)
  *   wise_full_attn_accum  dense causal attention + block mass (Eq. 2 and 5)
  *   wise_select_support   mass -> CSR block support (Section 5.1, Eq. 6)
+ *   wise_select_variant   temporal union and early-static controls (Eq. 18-22)
  *   wise_sparse_attn      attention inside the support (Section 5.2, Eq. 7-8)
  *
  * Conventions shared by every call
@@ -116,6 +117,43 @@ wise_status_t wise_select_support(const wise_attn_desc_t* desc, const float* mas
                                   int32_t n_steps, double eta, int32_t max_blocks,
                                   int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
                                   void* stream);
+
+/*
+ * Selection variants (same output contract as wise_select_support, no cap):
+ * the temporal-union working set of Section 5.1, Eq. (6) left-hand part and
+ * Appendix B, Eq. (18), and the early-static controls of Appendix B,
+ * Eq. (19)-(22).  They take single-step block masses r^(t) (each row sums to
+ * 1; one zeroed mass buffer per step given to wise_full_attn_accum):
+ *
+ * step_mass: fp32 [n_mass][batch][heads][n_blocks][n_blocks], read; entries
+ *            kb > q ignored.
+ * kind WISE_SELECT_UNION:        n_mass >= 1 steps (the paper: the last four
+ *     discovery steps); W = union over the steps of each step's own
+ *     eta-support (Eq. 6 right: smallest highest-mass set reaching eta, ties
+ *     to the lower block index).
+ * kind WISE_SELECT_STATIC:       n_mass == 1, the first step; W = its
+ *     eta-support (Static-95 with eta = 0.95, Eq. 19).
+ * kind WISE_SELECT_MASS_MATCHED: n_mass >= 2; step 0 is the first step,
+ *     steps 1.. the union window.  m = float64 sum of the first step's masses
+ *     over the union; W = smallest first-step-ranked set reaching m
+ *     (Eq. 20-21).
+ * kind WISE_SELECT_SIZE_MATCHED: n_mass >= 2 as above; W = the |union| blocks
+ *     of highest first-step mass (Eq. 22).
+ * Every result then gets the sink block 0 and the diagonal block q.
+ * eta in (0, 1]; col_capacity >= wise_select_max_nnz(desc, 0), else
+ * WISE_ERR_CAPACITY before any launch.  Invalid kind / n_mass ->
+ * WISE_ERR_INVALID_ARG.
+ */
+typedef enum {
+  WISE_SELECT_UNION = 1,
+  WISE_SELECT_STATIC = 2,
+  WISE_SELECT_MASS_MATCHED = 3,
+  WISE_SELECT_SIZE_MATCHED = 4
+} wise_select_kind_t;
+
+wise_status_t wise_select_variant(const wise_attn_desc_t* desc, int32_t kind, const float* step_mass,
+                                  int32_t n_mass, double eta, int32_t* row_ptr, int32_t* col_idx,
+                                  int64_t col_capacity, void* stream);
 
 /*
  * Reuse step, Section 5.2, Eq. (7)-(8): O = softmax(Q K^T * scale + M + R) V,

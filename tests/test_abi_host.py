@@ -31,8 +31,9 @@ def _declared_functions():
 
 def test_header_declares_expected_calls():
     names = _declared_functions()
-    for n in ("wise_full_attn", "wise_full_attn_accum", "wise_select_support", "wise_sparse_attn",
-              "wise_select_max_nnz", "wise_status_string", "wise_last_error", "wise_abi_version"):
+    for n in ("wise_full_attn", "wise_full_attn_accum", "wise_select_support", "wise_select_variant",
+              "wise_sparse_attn", "wise_select_max_nnz", "wise_status_string", "wise_last_error",
+              "wise_abi_version"):
         assert n in names
 
 
@@ -117,6 +118,32 @@ def test_select_arguments_rejected():
     assert sel(ctypes.byref(d), FAKE, 2, 0.9, 1, FAKE, FAKE, capped - 1, None) == wise.WISE_ERR_CAPACITY
     assert lib.wise_select_max_nnz(None, 0) == -1
     assert lib.wise_select_max_nnz(ctypes.byref(d), -3) == -1
+
+
+def test_select_variant_arguments_rejected():
+    lib = _lib()
+    d = _desc(s=256, blk=32)
+    sel = lib.wise_select_variant
+    need = lib.wise_select_max_nnz(ctypes.byref(d), 0)
+    ok_args = dict(union=(wise.SELECT_UNION, 4), static=(wise.SELECT_STATIC, 1),
+                   mass=(wise.SELECT_MASS_MATCHED, 5), size=(wise.SELECT_SIZE_MATCHED, 2))
+    for kind, n_mass in ok_args.values():
+        for eta in (0.0, 1.5, float("nan")):
+            assert sel(ctypes.byref(d), kind, FAKE, n_mass, eta, FAKE, FAKE, need, None) \
+                == wise.WISE_ERR_INVALID_ARG
+        assert sel(ctypes.byref(d), kind, None, n_mass, 0.9, FAKE, FAKE, need, None) \
+            == wise.WISE_ERR_INVALID_ARG
+        assert sel(ctypes.byref(d), kind, FAKE, n_mass, 0.9, FAKE, FAKE, need - 1, None) \
+            == wise.WISE_ERR_CAPACITY
+    # unknown kinds (0 is the main selection, which has its own call) and bad step counts
+    for kind in (0, 5, -1):
+        assert sel(ctypes.byref(d), kind, FAKE, 2, 0.9, FAKE, FAKE, need, None) == wise.WISE_ERR_INVALID_ARG
+    assert sel(ctypes.byref(d), wise.SELECT_UNION, FAKE, 0, 0.9, FAKE, FAKE, need, None) \
+        == wise.WISE_ERR_INVALID_ARG
+    assert sel(ctypes.byref(d), wise.SELECT_STATIC, FAKE, 2, 0.9, FAKE, FAKE, need, None) \
+        == wise.WISE_ERR_INVALID_ARG
+    for kind in (wise.SELECT_MASS_MATCHED, wise.SELECT_SIZE_MATCHED):
+        assert sel(ctypes.byref(d), kind, FAKE, 1, 0.9, FAKE, FAKE, need, None) == wise.WISE_ERR_INVALID_ARG
 
 
 def test_binding_refuses_cpu_tensors():
