@@ -44,6 +44,8 @@ def parse(argv=None):
     ap.add_argument("--cpu-heads", type=int, default=4)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB first (HBM counter calibration)")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the selection-variant figures (temporal union and the early-static controls)")
     ap.add_argument("--same-backend", action="store_true",
                     help="also time the sparse kernel on a full causal CSR")
     return ap.parse_args(argv)
@@ -276,6 +278,54 @@ def main(argv=None):
 
     med = lambda xs: float(np.median(xs))
     n_late = T - td
+
+    def timed_ms(fn, reps):
+        for _ in range(2):
+            fn()
+        out = []
+        for _ in range(reps):
+            ev[0].record(stream)
+            fn()
+            ev[1].record(stream)
+            ev[1].synchronize()
+            out.append(ev[0].elapsed_time(ev[1]))
+        return med(out)
+
+    # Selection variants on the same discovery steps: per-step masses (one
+    # zeroed buffer per step), the union over the last four discovery steps,
+    # and the early-static controls with the first step; then the late
+    # sparse launch on each variant's support.
+    variants = None
+    if not args.no_variants:
+        step_mass = torch.zeros(td, cfg.batch, cfg.heads, nb, nb, dtype=torch.float32, device=dev)
+        for t in range(td):
+            wise.wise_full_attn_accum(qs[t], ks[t], vs[t], step_mass[t], B, o=outs[t])
+        win = step_mass[td - min(4, td):td].contiguous()
+        first = step_mass[:1].contiguous()
+        ctrl = torch.cat([first, win]).contiguous()
+        vcap = wise.wise_select_max_nnz(cfg.batch, cfg.heads, cfg.seq_len, D, B, 0)
+        variants = {}
+        for name, kind, sm in (("union", wise.SELECT_UNION, win), ("static", wise.SELECT_STATIC, first),
+                               ("mass_matched", wise.SELECT_MASS_MATCHED, ctrl),
+                               ("size_matched", wise.SELECT_SIZE_MATCHED, ctrl)):
+            rp_v = torch.empty_like(row_ptr)
+            ci_v = torch.empty(max(vcap, 1), dtype=torch.int32, device=dev)
+            sel_ms = timed_ms(lambda: wise.wise_select_variant(kind, sm, cfg.eta, D, B, row_ptr=rp_v,
+                                                               col_idx=ci_v), 5)
+            fcv = flop_counts(cfg, rp_v.cpu().numpy())
+
+            def late_v():
+                for t in range(td, T):
+                    wise.wise_sparse_attn(qs[t], ks[t], vs[t], rp_v, ci_v, B, o=outs[t])
+            sp_ms = timed_ms(late_v, 3) / n_late
+            variants[name] = {"select_ms": round(sel_ms, 4),
+                              "density_admissible": round(fcv["density_adm"], 4),
+                              "sparse_ms": round(sp_ms, 4),
+                              "sparse_tflops_exec": round(fcv["sparse_exec"] / (sp_ms * 1e-3) / 1e12, 2),
+                              "steps": "union of steps %d..%d" % (td - min(4, td), td - 1) if name == "union"
+                              else ("step 0" if name == "static" else
+                                    "step 0 ranking; union of steps %d..%d" % (td - min(4, td), td - 1))}
+        del step_mass, win, first, ctrl
     k4_ms = med(per["k4"]) / n_late            # one sparse launch
     k1_ms = med(per["k1"]) / td                # one discovery launch (incl. the mass memset share)
     k3_ms = med(per["k3"])
@@ -328,6 +378,11 @@ def main(argv=None):
                      "compulsory_GBps": round(sparse_bytes(cfg, fc["nnz"], fc["n_rows"]) /
                                               (k4_ms * 1e-3) / 1e9, 1)},
     }
+    if variants is not None:
+        k2 = med(dts) / n_late
+        for vv in variants.values():
+            vv["late_step_speedup_vs_dense"] = round(k2 / vv["sparse_ms"], 3)
+        result["selection_variants"] = variants
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a sample (cpu_baseline)")
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_heads)
