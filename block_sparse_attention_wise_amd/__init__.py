@@ -47,7 +47,8 @@ class WiseError(RuntimeError):
 class WiseDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
                 ("seq_len", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("block_size", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+                ("block_size", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("kv_heads", ctypes.c_int32)]
 
 
 _lib = None
@@ -121,17 +122,22 @@ def _need(t, name, dtype, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
 
 
-def _desc(q, block_size: int, softmax_scale: float) -> WiseDesc:
+def _desc(q, block_size: int, softmax_scale: float, k=None) -> WiseDesc:
     b, h, s, d = q.shape
-    return WiseDesc(b, h, s, d, int(block_size), float(softmax_scale))
+    kv = int(k.shape[1]) if k is not None else 0
+    return WiseDesc(b, h, s, d, int(block_size), float(softmax_scale), kv)
 
 
 def _qkv(q, k, v):
+    """q [batch, heads, S, D]; k, v [batch, kv_heads, S, D] with kv_heads
+    dividing heads (grouped-query attention when smaller)."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, torch.bfloat16, 4)
-    if k.shape != q.shape or v.shape != q.shape:
-        raise ValueError(f"q/k/v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
+    b, h, s, d = q.shape
+    if (k.shape != v.shape or k.shape[0] != b or k.shape[2:] != q.shape[2:]
+            or k.shape[1] < 1 or h % k.shape[1] != 0):
+        raise ValueError(f"q/k/v shapes do not match: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
 
 
 def _out(o, q):
@@ -156,7 +162,7 @@ def wise_full_attn(q, k, v, block_size: int, o=None, lse=None, softmax_scale: fl
         if tuple(lse.shape) != tuple(q.shape[:3]):
             raise ValueError("lse must be [batch, heads, seq_len]")
         lse_ptr = lse.data_ptr()
-    d = _desc(q, block_size, softmax_scale)
+    d = _desc(q, block_size, softmax_scale, k)
     st = load_library().wise_full_attn(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                        o.data_ptr(), lse_ptr, _stream_ptr(stream))
     _check(st, "wise_full_attn")
@@ -178,7 +184,7 @@ def wise_full_attn_accum(q, k, v, mass, block_size: int, o=None, softmax_scale: 
     if tuple(mass.shape) != _mass_shape(q, block_size):
         raise ValueError(f"mass must be {_mass_shape(q, block_size)}, got {tuple(mass.shape)}")
     o = _out(o, q)
-    d = _desc(q, block_size, softmax_scale)
+    d = _desc(q, block_size, softmax_scale, k)
     st = load_library().wise_full_attn_accum(ctypes.byref(d), q.data_ptr(), k.data_ptr(),
                                              v.data_ptr(), o.data_ptr(), mass.data_ptr(),
                                              _stream_ptr(stream))
@@ -271,7 +277,7 @@ def wise_sparse_attn(q, k, v, row_ptr, col_idx, block_size: int, o=None,
     if row_ptr.numel() != b * h * (s // block_size) + 1:
         raise ValueError("row_ptr must have batch*heads*n_blocks + 1 entries")
     o = _out(o, q)
-    d = _desc(q, block_size, softmax_scale)
+    d = _desc(q, block_size, softmax_scale, k)
     st = load_library().wise_sparse_attn(ctypes.byref(d), q.data_ptr(), k.data_ptr(),
                                          v.data_ptr(), row_ptr.data_ptr(), col_idx.data_ptr(),
                                          o.data_ptr(), _stream_ptr(stream))

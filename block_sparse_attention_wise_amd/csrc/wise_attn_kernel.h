@@ -297,9 +297,12 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   float* slots = reinterpret_cast<float*>(extra);   // kMassTwoPass: [RPW][nblk][BLK/32]
 
   const size_t head_off = (size_t)bh * p.seq * D;
+  // grouped-query attention: query head h of batch entry b reads K/V head h / kv_group
+  const int kv_bh = (bh / p.heads) * (p.heads / p.kv_group) + (bh % p.heads) / p.kv_group;
+  const size_t kv_off = (size_t)kv_bh * p.seq * D;
   const uint16_t* Qh = p.q + head_off;
-  const uint16_t* Kh = p.k + head_off;
-  const uint16_t* Vh = p.v + head_off;
+  const uint16_t* Kh = p.k + kv_off;
+  const uint16_t* Vh = p.v + kv_off;
   const int qrow = qb * BLK + wr * 32 + n;
 
   bf16x8_t qf[Sh::kChunks];

@@ -69,6 +69,8 @@ wise_status_t check_desc(const wise_attn_desc_t* d, int32_t* nblk, int64_t* n_ro
     return fail(WISE_ERR_UNSUPPORTED, "seq_len %d above 65536", d->seq_len);
   if (!std::isfinite(d->softmax_scale))
     return fail(WISE_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (d->kv_heads < 0 || (d->kv_heads > 0 && d->heads % d->kv_heads != 0))
+    return fail(WISE_ERR_INVALID_ARG, "kv_heads %d must be 0 or divide heads %d", d->kv_heads, d->heads);
   const int64_t heads_total = (int64_t)d->batch * d->heads;
   const int64_t rows = heads_total * (d->seq_len / d->block_size);
   if (rows >= (int64_t)INT32_MAX)
@@ -122,6 +124,8 @@ wise_status_t run_attn(const wise_attn_desc_t* d, int mode, const void* q, const
   p.row_ptr = row_ptr;
   p.col_idx = col_idx;
   p.heads_total = d->batch * d->heads;
+  p.heads = d->heads;
+  p.kv_group = d->kv_heads > 0 ? d->heads / d->kv_heads : 1;
   p.seq = d->seq_len;
   p.nblk = nblk;
   p.scale_log2 = scale_log2(d);

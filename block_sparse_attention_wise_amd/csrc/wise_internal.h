@@ -26,6 +26,8 @@ struct AttnParams {
   const int32_t* row_ptr;  // kSparse only
   const int32_t* col_idx;  // kSparse only
   int32_t heads_total;     // batch * heads
+  int32_t heads;           // query heads per batch entry
+  int32_t kv_group;        // query heads per K/V head (1: one K/V head each)
   int32_t seq;
   int32_t nblk;            // seq / block
   float scale_log2;        // softmax scale * log2(e)

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define WISE_ABI_VERSION 1
+#define WISE_ABI_VERSION 2
 
 typedef enum {
   WISE_OK = 0,
@@ -60,18 +60,23 @@ typedef enum {
 /* Shape of one attention call.  All tensors of a call share it. */
 typedef struct {
   int32_t batch;       /* >= 1                                         */
-  int32_t heads;       /* >= 1; Q, K and V have the same head count    */
+  int32_t heads;       /* >= 1 query heads (Q, O, mass and CSR rows)   */
   int32_t seq_len;     /* >= block_size, multiple of block_size         */
   int32_t head_dim;    /* 64, 96 or 128                                 */
   int32_t block_size;  /* B of Section 5.1: 32, 64 or 128               */
   float softmax_scale; /* <= 0 selects 1/sqrt(head_dim)                 */
+  int32_t kv_heads;    /* K/V heads: 0 (= heads) or a divisor of heads;
+                          query head h reads K/V head h / (heads / kv_heads)
+                          (grouped-query attention)                     */
 } wise_attn_desc_t;
 
 /*
  * Dense causal attention, Eq. (2): O = softmax(Q K^T * scale + M) V.
  *
- * q, k, v: bf16 [batch][heads][seq_len][head_dim] (read).
- * o:       bf16, same layout (written, rounded to nearest even).
+ * q:       bf16 [batch][heads][seq_len][head_dim] (read).
+ * k, v:    bf16 [batch][kv_heads][seq_len][head_dim] (read; kv_heads as in
+ *          the descriptor, heads when it is 0).
+ * o:       bf16, q's layout (written, rounded to nearest even).
  * lse:     optional (NULL to skip) fp32 [batch][heads][seq_len]; receives
  *          the natural-log row normaliser log(sum_j exp(score_ij)).
  * This is the dense baseline that the late steps are compared against.

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = _lib()
-    assert lib.wise_abi_version() == 1
+    assert lib.wise_abi_version() == 2
     assert lib.wise_status_string(0) == b"WISE_OK"
     assert lib.wise_status_string(3) == b"WISE_ERR_CAPACITY"
     assert lib.wise_status_string(99) == b"WISE_ERR_UNKNOWN"
@@ -118,6 +118,16 @@ def test_select_arguments_rejected():
     assert sel(ctypes.byref(d), FAKE, 2, 0.9, 1, FAKE, FAKE, capped - 1, None) == wise.WISE_ERR_CAPACITY
     assert lib.wise_select_max_nnz(None, 0) == -1
     assert lib.wise_select_max_nnz(ctypes.byref(d), -3) == -1
+
+
+def test_gqa_descriptor_rejected_when_heads_do_not_split():
+    lib = _lib()
+    for kv in (3, -1, 5):
+        d = _desc(h=4)
+        d.kv_heads = kv
+        assert lib.wise_full_attn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None) \
+            == wise.WISE_ERR_INVALID_ARG, kv
+    assert lib.wise_abi_version() == 2
 
 
 def test_select_variant_arguments_rejected():

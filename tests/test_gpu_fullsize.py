@@ -39,7 +39,7 @@ def _samples(cfg, rng):
     return out
 
 
-@pytest.mark.parametrize("name", ["ctx4k", "ctx8k", "ctx16k", "ctx32k", "wide", "long"])
+@pytest.mark.parametrize("name", ["ctx4k", "ctx8k", "ctx16k", "ctx32k", "wide", "long", "gqa4k"])
 def test_full_size_trajectory(name):
     cfg = CONFIGS[name]
     n_steps = cfg.steps if name == "ctx4k" else cfg.td + 2

@@ -379,3 +379,52 @@ def test_accum_long_rows_matches_oracle(shape):
                                     f"O t{t} b{b}h{h}q{qb}")
             err = np.abs(mass_h[b, h][qbs] - ref)
             assert err.max() <= mass_tolerance(2), err.max()
+
+
+# Grouped-query attention: (batch, heads, kv_heads, seq, head_dim, block).
+GQA_SHAPES = [
+    (1, 8, 2, 320, 128, 64),
+    (2, 4, 1, 256, 64, 32),
+    (1, 6, 3, 384, 96, 128),
+]
+
+
+@pytest.mark.parametrize("shape", GQA_SHAPES, ids=[f"b{s[0]}h{s[1]}kv{s[2]}s{s[3]}d{s[4]}B{s[5]}" for s in GQA_SHAPES])
+def test_gqa_all_calls_match_oracle(shape):
+    """Every attention call with K/V shared by groups of query heads: query
+    head h reads K/V head h // (heads / kv_heads); mass and CSR rows stay per
+    query head."""
+    b_, h_, kv_, s_, d_, blk = shape
+    say(f"gqa {shape}")
+    cfg = _cfg(b_, h_, s_, d_, blk).with_(kv_heads=kv_, td=2, steps=3)
+    steps = _steps(cfg)
+    G, nb = h_ // kv_, s_ // blk
+    assert steps[0][2].shape[1] == kv_
+    mass = torch.zeros(b_, h_, nb, nb, dtype=torch.float32, device="cuda")
+    dense, accum = [], []
+    for t, q, k, v in steps[:2]:
+        qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+        dense.append(bf16_dev_to_f64(wise.wise_full_attn(qd, kd, vd, blk)))
+        accum.append(bf16_dev_to_f64(wise.wise_full_attn_accum(qd, kd, vd, mass, blk)))
+    rp, ci = wise.wise_select_support(mass, 2, cfg.eta, d_, blk)
+    _, q, k, v = steps[2]
+    sparse = bf16_dev_to_f64(wise.wise_sparse_attn(to_dev(q), to_dev(k), to_dev(v), rp, ci, blk))
+    torch.cuda.synchronize()
+    rows = csr_rows(rp.cpu().numpy(), ci.cpu().numpy())
+    mass_h = mass.cpu().numpy().astype(np.float64)
+    sc = oracle.default_scale(d_)
+    for b in range(b_):
+        for h in range(h_):
+            ref_mass = np.zeros((nb, nb))
+            for t in range(2):
+                _, q, k, v = steps[t]
+                Q, K, V = _oracle_head(q, b, h), _oracle_head(k, b, h // G), _oracle_head(v, b, h // G)
+                ref = oracle.dense_attention(Q, K, V, sc)
+                compare_outputs(dense[t][b, h], ref, f"dense t{t} b{b}h{h}")
+                compare_outputs(accum[t][b, h], ref, f"accum t{t} b{b}h{h}")
+                ref_mass += oracle.block_mass(Q, K, sc, blk)
+            assert np.abs(mass_h[b, h] - ref_mass).max() <= mass_tolerance(2)
+            _, q, k, v = steps[2]
+            Q, K, V = _oracle_head(q, b, h), _oracle_head(k, b, h // G), _oracle_head(v, b, h // G)
+            sup = {qb: rows[(b * h_ + h) * nb + qb] for qb in range(nb)}
+            compare_outputs(sparse[b, h], oracle.masked_attention(Q, K, V, sup, blk, sc), f"sparse b{b}h{h}")

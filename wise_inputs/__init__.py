@@ -20,6 +20,9 @@ synthetic inputs stand in for their shapes only):
   different query blocks add up.  Optionally each other off-diagonal,
   non-sink block also gets a ``random_beta`` shift with probability
   ``random_frac``;
+* grouped-query attention (``kv_heads`` < ``heads``): query head h reads
+  key/value head h // (heads / kv_heads); each key head receives the planted
+  shifts of every query head of its group (they add up, as above);
 * drift: X(t) = X(t-1) + sigma * N(0, 1) for t >= 1 (fp32 random walk);
 * handoff: every step is rounded to bf16 (round-to-nearest-even) and passed as
   raw uint16 bits, identical for the GPU and for the oracle.
@@ -58,10 +61,20 @@ class WorkloadConfig:
     random_frac: float = 0.0
     random_beta: float = 0.0
     index: int = 0      # seed offset
+    kv_heads: int = 0   # key/value heads (0: one per query head)
 
     @property
     def n_blocks(self) -> int:
         return self.seq_len // self.block
+
+    @property
+    def n_kv(self) -> int:
+        return self.kv_heads or self.heads
+
+    @property
+    def group(self) -> int:
+        """Query heads per key/value head."""
+        return self.heads // self.n_kv
 
     @property
     def seed(self) -> int:
@@ -99,6 +112,10 @@ CONFIGS = {
     "long": _cfg("long", 4, batch=1, heads=40, head_dim=128, seq_len=32768,
                  block=128, steps=16, td=4, eta=0.90, cap=64, planted=(12, 12),
                  beta=2.0, sigma=0.02, random_frac=0.02, random_beta=0.5),
+    # Recurrent-Llama-like grouped-query geometry: 32 query heads, 8 KV heads.
+    "gqa4k": _cfg("gqa4k", 5, batch=1, heads=32, kv_heads=8, head_dim=128, seq_len=4096,
+                  block=64, steps=32, td=8, eta=0.90, cap=0, planted=(8, 8),
+                  beta=2.0, sigma=0.02),
 }
 
 
@@ -155,54 +172,91 @@ class Workload:
         self.cfg = cfg
         self.threads = max(1, threads)
 
-    # ---- one (batch, head) -------------------------------------------------
-    def head_base(self, b: int, h: int):
+    # ---- base tensors --------------------------------------------------------
+    def q_base(self, b: int, h: int) -> np.ndarray:
+        return _normal(self.cfg, _TENSOR_Q, b, h, 0)
+
+    def kv_base(self, b: int, g: int, q0s=None):
+        """[k0, v0] of key/value head g; q0s: the base queries of its query
+        heads g*G .. g*G+G-1 (generated when not given)."""
         cfg = self.cfg
-        q0 = _normal(cfg, _TENSOR_Q, b, h, 0)
-        k0 = _normal(cfg, _TENSOR_K, b, h, 0)
-        v0 = _normal(cfg, _TENSOR_V, b, h, 0)
-        k0 = k0 + _plant_shift(cfg, b, h, q0)
-        return [q0, k0, v0]
+        G = cfg.group
+        if q0s is None:
+            q0s = [self.q_base(b, g * G + i) for i in range(G)]
+        k0 = _normal(cfg, _TENSOR_K, b, g, 0)
+        for i in range(G):
+            k0 = k0 + _plant_shift(cfg, b, g * G + i, q0s[i])
+        v0 = _normal(cfg, _TENSOR_V, b, g, 0)
+        return [k0, v0]
 
-    def _drift(self, masters, b, h, step):
-        s = np.float32(self.cfg.sigma)
-        for i, tensor in enumerate((_TENSOR_Q, _TENSOR_K, _TENSOR_V)):
-            masters[i] = masters[i] + s * _normal(self.cfg, tensor, b, h, step)
+    def head_base(self, b: int, h: int):
+        """[q0, k0, v0] seen by query head h."""
+        G = self.cfg.group
+        g = h // G
+        q0s = [self.q_base(b, g * G + i) for i in range(G)]
+        return [q0s[h - g * G]] + self.kv_base(b, g, q0s)
 
-    def head_step(self, b: int, h: int, t: int):
-        """bf16 bits (q, k, v), each [S, D], of (batch b, head h) at step t."""
-        masters = self.head_base(b, h)
-        for step in range(1, t + 1):
-            self._drift(masters, b, h, step)
-        return tuple(round_to_bf16_bits(m) for m in masters)
+    def _drift_one(self, master, tensor, b, hh, step):
+        return master + np.float32(self.cfg.sigma) * _normal(self.cfg, tensor, b, hh, step)
 
     def head_steps(self, b: int, h: int, steps=None):
-        """Iterate (t, (q, k, v) bits) over steps of one head."""
-        T = self.cfg.steps if steps is None else steps
-        masters = self.head_base(b, h)
+        """Iterate (t, (q, k, v) bits) over steps of one query head (k, v of
+        its key/value head)."""
+        cfg = self.cfg
+        T = cfg.steps if steps is None else steps
+        g = h // cfg.group
+        q, k, v = self.head_base(b, h)
         for t in range(T):
             if t > 0:
-                self._drift(masters, b, h, t)
-            yield t, tuple(round_to_bf16_bits(m) for m in masters)
+                q = self._drift_one(q, _TENSOR_Q, b, h, t)
+                k = self._drift_one(k, _TENSOR_K, b, g, t)
+                v = self._drift_one(v, _TENSOR_V, b, g, t)
+            yield t, tuple(round_to_bf16_bits(m) for m in (q, k, v))
+
+    def head_step(self, b: int, h: int, t: int):
+        """bf16 bits (q, k, v), each [S, D], of (batch b, query head h) at step t."""
+        for tt, qkv in self.head_steps(b, h, t + 1):
+            if tt == t:
+                return qkv
 
     # ---- whole tensors --------------------------------------------------------
     def steps(self, n_steps: Optional[int] = None) -> Iterator[Tuple[int, np.ndarray, np.ndarray, np.ndarray]]:
-        """Iterate (t, q, k, v) with bf16 bits shaped [batch, heads, S, D]."""
+        """Iterate (t, q, k, v) with bf16 bits shaped [batch, heads, S, D] (q)
+        and [batch, kv_heads, S, D] (k, v)."""
         cfg = self.cfg
         T = cfg.steps if n_steps is None else n_steps
-        units = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
-        shape = (cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim)
+        G = cfg.group
+        groups = [(b, g) for b in range(cfg.batch) for g in range(cfg.n_kv)]
+        qshape = (cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim)
+        kvshape = (cfg.batch, cfg.n_kv, cfg.seq_len, cfg.head_dim)
         with ThreadPoolExecutor(self.threads) as pool:
-            masters = list(pool.map(lambda u: self.head_base(*u), units))
+            def base(u):
+                b, g = u
+                q0s = [self.q_base(b, g * G + i) for i in range(G)]
+                return q0s + self.kv_base(b, g, q0s)      # G queries, then k, v
+            masters = list(pool.map(base, groups))
+
+            def drift(iu, t):
+                i, (b, g) = iu
+                m = masters[i]
+                for j in range(G):
+                    m[j] = self._drift_one(m[j], _TENSOR_Q, b, g * G + j, t)
+                m[G] = self._drift_one(m[G], _TENSOR_K, b, g, t)
+                m[G + 1] = self._drift_one(m[G + 1], _TENSOR_V, b, g, t)
+
             for t in range(T):
                 if t > 0:
-                    list(pool.map(lambda iu: self._drift(masters[iu[0]], iu[1][0], iu[1][1], t),
-                                  enumerate(units)))
-                out = [np.empty(shape, dtype=np.uint16) for _ in range(3)]
+                    list(pool.map(lambda iu: drift(iu, t), enumerate(groups)))
+                qo = np.empty(qshape, dtype=np.uint16)
+                ko = np.empty(kvshape, dtype=np.uint16)
+                vo = np.empty(kvshape, dtype=np.uint16)
 
                 def _round(iu):
-                    i, (b, h) = iu
-                    for j in range(3):
-                        out[j][b, h] = round_to_bf16_bits(masters[i][j])
-                list(pool.map(_round, enumerate(units)))
-                yield t, out[0], out[1], out[2]
+                    i, (b, g) = iu
+                    m = masters[i]
+                    for j in range(G):
+                        qo[b, g * G + j] = round_to_bf16_bits(m[j])
+                    ko[b, g] = round_to_bf16_bits(m[G])
+                    vo[b, g] = round_to_bf16_bits(m[G + 1])
+                list(pool.map(_round, enumerate(groups)))
+                yield t, qo, ko, vo
