@@ -22,6 +22,7 @@ from typing import Optional, Tuple
 __all__ = ["WiseError", "WiseDesc", "load_library", "library_path", "wise_full_attn",
            "wise_full_attn_accum", "wise_select_support", "wise_select_variant", "wise_sparse_attn",
            "SELECT_UNION", "SELECT_STATIC", "SELECT_MASS_MATCHED", "SELECT_SIZE_MATCHED",
+           "wise_support_mass", "wise_support_overlap",
            "wise_select_max_nnz", "wise_abi_version", "WISE_OK", "WISE_ERR_INVALID_ARG",
            "WISE_ERR_UNSUPPORTED", "WISE_ERR_CAPACITY", "WISE_ERR_HIP"]
 
@@ -71,6 +72,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "wise_full_attn_accum": ([dp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "wise_select_support": ([dp, vp, i32, ctypes.c_double, i32, vp, vp, i64, vp], ctypes.c_int),
         "wise_select_variant": ([dp, i32, vp, i32, ctypes.c_double, vp, vp, i64, vp], ctypes.c_int),
+        "wise_support_mass": ([dp, vp, vp, vp, vp, vp], ctypes.c_int),
+        "wise_support_overlap": ([dp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "wise_sparse_attn": ([dp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "wise_select_max_nnz": ([dp, i32], i64),
         "wise_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -264,6 +267,47 @@ def wise_select_variant(kind: int, step_mass, eta: float, head_dim: int, block_s
                                             col_idx.numel(), _stream_ptr(stream))
     _check(st, "wise_select_variant")
     return row_ptr, col_idx
+
+
+def wise_support_mass(mass, row_ptr, col_idx, head_dim: int, block_size: int, retained=None, stream=None):
+    """Per-row mass of ``mass`` [batch, heads, nB, nB] inside the CSR support
+    -> fp32 [batch * heads * nB] (retained future attention mass)."""
+    torch = _torch()
+    _need(mass, "mass", torch.float32, 4)
+    _need(row_ptr, "row_ptr", torch.int32, 1)
+    _need(col_idx, "col_idx", torch.int32, 1)
+    b, h, nb, _ = mass.shape
+    n_rows = b * h * nb
+    if row_ptr.numel() != n_rows + 1:
+        raise ValueError(f"row_ptr must have {n_rows + 1} entries")
+    if retained is None:
+        retained = torch.empty(n_rows, dtype=torch.float32, device=mass.device)
+    _need(retained, "retained", torch.float32, 1)
+    d = WiseDesc(b, h, nb * block_size, head_dim, block_size, 0.0)
+    st = load_library().wise_support_mass(ctypes.byref(d), mass.data_ptr(), row_ptr.data_ptr(),
+                                          col_idx.data_ptr(), retained.data_ptr(), _stream_ptr(stream))
+    _check(st, "wise_support_mass")
+    return retained
+
+
+def wise_support_overlap(csr_a, csr_b, batch: int, heads: int, n_blocks: int, head_dim: int,
+                         block_size: int, stream=None):
+    """Per-row |A & B| and |A | B| of two CSR supports -> (n_inter, n_union) int32."""
+    torch = _torch()
+    (ra, ca), (rb, cb) = csr_a, csr_b
+    for t, n in ((ra, "row_ptr_a"), (ca, "col_idx_a"), (rb, "row_ptr_b"), (cb, "col_idx_b")):
+        _need(t, n, torch.int32, 1)
+    n_rows = batch * heads * n_blocks
+    if ra.numel() != n_rows + 1 or rb.numel() != n_rows + 1:
+        raise ValueError(f"row_ptr arrays must have {n_rows + 1} entries")
+    inter = torch.empty(n_rows, dtype=torch.int32, device=ra.device)
+    uni = torch.empty(n_rows, dtype=torch.int32, device=ra.device)
+    d = WiseDesc(batch, heads, n_blocks * block_size, head_dim, block_size, 0.0)
+    st = load_library().wise_support_overlap(ctypes.byref(d), ra.data_ptr(), ca.data_ptr(), rb.data_ptr(),
+                                             cb.data_ptr(), inter.data_ptr(), uni.data_ptr(),
+                                             _stream_ptr(stream))
+    _check(st, "wise_support_overlap")
+    return inter, uni
 
 
 def wise_sparse_attn(q, k, v, row_ptr, col_idx, block_size: int, o=None,

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libwise.so")
-SOURCES = ["wise_capi.hip", "wise_select.hip", "wise_attn_d64.hip", "wise_attn_d96.hip",
+SOURCES = ["wise_capi.hip", "wise_select.hip", "wise_diag.hip", "wise_attn_d64.hip", "wise_attn_d96.hip",
            "wise_attn_d128.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -252,6 +252,45 @@ wise_status_t wise_select_variant(const wise_attn_desc_t* desc, int32_t kind, co
   return ok();
 }
 
+wise_status_t wise_support_mass(const wise_attn_desc_t* desc, const float* mass, const int32_t* row_ptr,
+                                const int32_t* col_idx, float* retained, void* stream) {
+  int32_t nblk;
+  int64_t n_rows;
+  wise_status_t st = check_desc(desc, &nblk, &n_rows);
+  if (st != WISE_OK) return st;
+  if (mass == nullptr || row_ptr == nullptr || col_idx == nullptr || retained == nullptr)
+    return fail(WISE_ERR_INVALID_ARG, "mass / row_ptr / col_idx / retained is NULL");
+  if ((reinterpret_cast<uintptr_t>(mass) | reinterpret_cast<uintptr_t>(row_ptr) |
+       reinterpret_cast<uintptr_t>(col_idx) | reinterpret_cast<uintptr_t>(retained)) & 3u)
+    return fail(WISE_ERR_INVALID_ARG, "mass / row_ptr / col_idx / retained not 4-byte aligned");
+  if (nblk > 64 * 32) return fail(WISE_ERR_UNSUPPORTED, "n_blocks %d above 2048", nblk);
+  const hipError_t e = launch_support_mass(mass, row_ptr, col_idx, retained, (int)n_rows, nblk,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(WISE_ERR_HIP, "support-mass launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+wise_status_t wise_support_overlap(const wise_attn_desc_t* desc, const int32_t* row_ptr_a,
+                                   const int32_t* col_idx_a, const int32_t* row_ptr_b, const int32_t* col_idx_b,
+                                   int32_t* n_inter, int32_t* n_union, void* stream) {
+  int32_t nblk;
+  int64_t n_rows;
+  wise_status_t st = check_desc(desc, &nblk, &n_rows);
+  if (st != WISE_OK) return st;
+  if (row_ptr_a == nullptr || col_idx_a == nullptr || row_ptr_b == nullptr || col_idx_b == nullptr ||
+      n_inter == nullptr || n_union == nullptr)
+    return fail(WISE_ERR_INVALID_ARG, "a CSR array or an output is NULL");
+  if ((reinterpret_cast<uintptr_t>(row_ptr_a) | reinterpret_cast<uintptr_t>(col_idx_a) |
+       reinterpret_cast<uintptr_t>(row_ptr_b) | reinterpret_cast<uintptr_t>(col_idx_b) |
+       reinterpret_cast<uintptr_t>(n_inter) | reinterpret_cast<uintptr_t>(n_union)) & 3u)
+    return fail(WISE_ERR_INVALID_ARG, "CSR arrays / outputs not 4-byte aligned");
+  if (nblk > 64 * 32) return fail(WISE_ERR_UNSUPPORTED, "n_blocks %d above 2048", nblk);
+  const hipError_t e = launch_support_overlap(row_ptr_a, col_idx_a, row_ptr_b, col_idx_b, n_inter, n_union,
+                                              (int)n_rows, nblk, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(WISE_ERR_HIP, "support-overlap launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* wise_status_string(wise_status_t status) {
   switch (status) {
     case WISE_OK: return "WISE_OK";

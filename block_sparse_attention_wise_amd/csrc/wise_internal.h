@@ -76,6 +76,13 @@ struct SelectParams {
 
 hipError_t launch_select(const SelectParams& p, hipStream_t stream);
 
+// Diagnostics: retained mass of a support, and per-row overlap of two supports.
+hipError_t launch_support_mass(const float* mass, const int32_t* row_ptr, const int32_t* col_idx, float* out,
+                               int n_rows, int nblk, hipStream_t stream);
+hipError_t launch_support_overlap(const int32_t* rp_a, const int32_t* ci_a, const int32_t* rp_b,
+                                  const int32_t* ci_b, int32_t* inter, int32_t* uni, int n_rows, int nblk,
+                                  hipStream_t stream);
+
 // LDS budget of one workgroup on gfx950.
 constexpr size_t kMaxLds = 160 * 1024;
 

@@ -12,6 +12,8 @@
  *   wise_full_attn_accum  dense causal attention + block mass (Eq. 2 and 5)
  *   wise_select_support   mass -> CSR block support (Section 5.1, Eq. 6)
  *   wise_select_variant   temporal union and early-static controls (Eq. 18-22)
+ *   wise_support_mass     retained attention mass of a support (diagnostic)
+ *   wise_support_overlap  per-row overlap of two supports (Jaccard, Eq. 24-25)
  *   wise_sparse_attn      attention inside the support (Section 5.2, Eq. 7-8)
  *
  * Conventions shared by every call
@@ -177,6 +179,31 @@ wise_status_t wise_select_variant(const wise_attn_desc_t* desc, int32_t kind, co
 wise_status_t wise_sparse_attn(const wise_attn_desc_t* desc, const void* q, const void* k,
                                const void* v, const int32_t* row_ptr, const int32_t* col_idx,
                                void* o, void* stream);
+
+/*
+ * Diagnostics of the frozen working set (Section 7, "Evaluation metrics";
+ * Appendix C.2, Eq. 23-25).  CSR rows are read as sets, as in
+ * wise_sparse_attn.
+ *
+ * wise_support_mass: retained[r] = sum over kb in row r's support of
+ *   mass[r][kb] (float64 sum in block order, stored fp32).  With the block
+ *   masses of an unrestricted step t > td (wise_full_attn_accum into a zeroed
+ *   buffer), this is the retained future attention mass of the row; the
+ *   method's figure is its mean over rows and late steps.
+ *   mass: fp32 [batch][heads][n_blocks][n_blocks] (read);
+ *   retained: fp32 [batch * heads * n_blocks] (written).
+ *
+ * wise_support_overlap: n_inter[r] = |A_r intersect B_r|, n_union[r] =
+ *   |A_r union B_r| for two CSRs A and B over the same rows.  The Jaccard
+ *   similarity of Eq. (24)/(25) for one batch element is the sum of n_inter
+ *   over its rows divided by the sum of n_union.
+ *   n_inter, n_union: int32 [batch * heads * n_blocks] (written).
+ */
+wise_status_t wise_support_mass(const wise_attn_desc_t* desc, const float* mass, const int32_t* row_ptr,
+                                const int32_t* col_idx, float* retained, void* stream);
+wise_status_t wise_support_overlap(const wise_attn_desc_t* desc, const int32_t* row_ptr_a,
+                                   const int32_t* col_idx_a, const int32_t* row_ptr_b, const int32_t* col_idx_b,
+                                   int32_t* n_inter, int32_t* n_union, void* stream);
 
 /* Upper bound of the CSR size wise_select_support can write:
  * sum over rows of min(q + 1, max_blocks + 2) (q + 1 when max_blocks == 0).

@@ -21,6 +21,9 @@ out in float64 with numpy, in the order the paper states it:
   softmax(Q K^T / sqrt(d_h) + M + R) V.
 * Appendix A.1, Eq. (13): identification margins delta_rank, delta_minus,
   delta_plus and Delta_q, used to tell near-tie rows from decided ones.
+* Section 7 ("Evaluation metrics") and Appendix C.2, Eq. (23)-(25):
+  retained future attention mass of a frozen support, the rolling working
+  set and the Jaccard similarity of two working-set collections.
 
 Readings where the paper leaves a step open (all of them also written out
 with their reasons in the design notes):
@@ -44,6 +47,10 @@ with their reasons in the design notes):
    "the first recurrent step" of the controls is the first discovery step
    (0-based step 0).  m_q^WISE and K_q of Eq. (20) and (22) are taken over the
    union's eta-ranked part, and m_q^WISE is summed in float64.
+8. Diagnostics use the working sets as the method builds them (sink and
+   diagonal included); Eq. (23)'s window max(1, t-3)..t is max(0, t-3)..t
+   with 0-based steps; the Jaccard of Eq. (24)/(25) pools the (row, key
+   block) pairs of one example before dividing.
 
 Inputs are float64 arrays (``bf16_to_f64`` widens bf16 bits exactly).
 """
@@ -59,7 +66,8 @@ __all__ = [
     "dense_attention", "block_mass", "block_mass_rows", "mean_block_mass",
     "select_support", "support_margins", "working_set_mask",
     "eta_support", "topk_support", "select_union", "select_static",
-    "select_mass_matched", "select_size_matched",
+    "select_mass_matched", "select_size_matched", "retained_mass",
+    "rolling_working_set", "jaccard",
     "masked_attention_weights", "masked_attention", "trajectory_head",
 ]
 
@@ -253,6 +261,34 @@ def support_margins(mbar_row, q: int, eta: float) -> Dict[str, float]:
                 d_plus / k_star)
     return {"k_star": k_star, "delta_rank": d_rank, "delta_minus": d_minus,
             "delta_plus": d_plus, "Delta": delta}
+
+
+def retained_mass(mass_row, support_row: Sequence[int], q: int) -> float:
+    """Retained attention mass (Section 7): the part of one step's block
+    masses r_qb (Eq. 5; they sum to 1 over the admissible blocks) that falls
+    inside the support; entries outside [0, q] and repeats are ignored."""
+    total = 0.0
+    for b in sorted(set(int(x) for x in support_row)):
+        if 0 <= b <= q:
+            total += float(mass_row[b])
+    return total
+
+
+def rolling_working_set(step_rows, t: int, q: int, eta: float) -> List[int]:
+    """Eq. (23): the union of the per-step eta-supports of steps
+    max(0, t-3)..t (0-based), plus sink and diagonal (reading 8)."""
+    return select_union(list(step_rows)[max(0, t - 3):t + 1], q, eta)
+
+
+def jaccard(rows_a: Sequence[Sequence[int]], rows_b: Sequence[Sequence[int]]) -> float:
+    """Eq. (24)/(25) for one example: the working-set collections are the
+    sets of (row, key block) pairs; |A & B| / |A | B| over all rows pooled."""
+    inter = union = 0
+    for a, b in zip(rows_a, rows_b):
+        sa, sb = set(a), set(b)
+        inter += len(sa & sb)
+        union += len(sa | sb)
+    return inter / union if union else 1.0
 
 
 def working_set_mask(support_row: Sequence[int], S: int, block: int, rows) -> np.ndarray:

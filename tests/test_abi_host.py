@@ -168,3 +168,41 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(wise, "_lib", None)
     with pytest.raises(ImportError):
         wise.load_library(str(tmp_path / "missing.so"))
+
+
+def test_m0_only_feeds_the_direct_lds_loads():
+    """The attention kernels write M0 from inline assembly right before each
+    buffer_load ... lds (the compiler is not told about those LDS writes).
+    That is only sound while nothing else in the kernels uses M0: check the
+    generated gfx950 assembly."""
+    import shutil
+    import subprocess
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+    hipcc = "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    csrc = os.path.join(ROOT, "block_sparse_attention_wise_amd", "csrc")
+    tmp = tempfile.mkdtemp()
+
+    def asm(name):
+        out = os.path.join(tmp, name + ".s")
+        subprocess.run([hipcc, "--offload-arch=gfx950", "-O3", "-std=c++20", "-Xclang", "-target-feature",
+                        "-Xclang", "-packed-fp32-ops", "-S", "--cuda-device-only",
+                        os.path.join(csrc, name + ".hip"), "-o", out],
+                       check=True, capture_output=True)
+        return open(out).read().splitlines()
+    try:
+        with ThreadPoolExecutor(3) as pool:
+            listings = list(pool.map(asm, ["wise_attn_d64", "wise_attn_d96", "wise_attn_d128"]))
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    n_dma = 0
+    for lines in listings:
+        body = [l.strip() for l in lines if l.strip() and not l.strip().startswith(";")]
+        for i, l in enumerate(body):
+            if re.search(r"\bm0\b", l):
+                assert l.startswith("s_mov_b32 m0, s"), l
+                assert body[i + 1].startswith("buffer_load_dwordx4") and body[i + 1].endswith(" lds"), body[i + 1]
+                n_dma += 1
+    assert n_dma > 0

@@ -33,7 +33,10 @@ def _impl(**over):
                          select_union=oracle.select_union,
                          select_static=oracle.select_static,
                          select_mass_matched=oracle.select_mass_matched,
-                         select_size_matched=oracle.select_size_matched)
+                         select_size_matched=oracle.select_size_matched,
+                         retained_mass=oracle.retained_mass,
+                         rolling_working_set=oracle.rolling_working_set,
+                         jaccard=oracle.jaccard)
     for k, v in over.items():
         setattr(ns, k, v)
     return ns
@@ -379,6 +382,45 @@ def pin_matched_controls(impl):
         assert sm == sorted(set(order[:len(union)]) | {0, q}), (trial, sm)
 
 
+def pin_retained_mass(impl):
+    """Section 7: the full admissible support retains all of a step's mass
+    (Eq. 5 rows sum to 1); at Q = 0 the sink + diagonal support retains the
+    closed-form r_q0 + r_qq; invalid and repeated entries change nothing."""
+    S, D, B = 128, 8, 16
+    nb = S // B
+    q0 = np.zeros((S, D))
+    k0 = np.random.default_rng(31).standard_normal((S, D))
+    r = oracle.block_mass(q0, k0, 1.0, B)
+    for qb in range(nb):
+        assert abs(impl.retained_mass(r[qb], list(range(qb + 1)), qb) - 1.0) < 1e-12
+        i = np.arange(qb * B, (qb + 1) * B)
+        closed_sink = float(np.mean([min(B, ii + 1) / (ii + 1) for ii in i]))
+        closed_diag = float(np.mean([(ii - qb * B + 1) / (ii + 1) for ii in i]))
+        want = closed_sink if qb == 0 else closed_sink + closed_diag
+        assert abs(impl.retained_mass(r[qb], [0, qb], qb) - want) < 1e-12, qb
+        assert impl.retained_mass(r[qb], [qb, 0, 0, -1, qb + 1, qb], qb) == impl.retained_mass(r[qb], [0, qb], qb)
+
+
+def pin_rolling_and_jaccard(impl):
+    """Eq. (23)-(24): rolling sets from the dyadic fixture's windows, and a
+    hand-worked pooled Jaccard (per-row averaging would give 0.75)."""
+    with open(os.path.join(GOLDEN, "selection_variants_dyadic.json")) as f:
+        case = json.load(f)["cases"][0]
+    q, eta = case["q"], case["eta"]
+    steps = [np.array(case["first"])] + [np.array(w) for w in case["window"]]
+    assert impl.rolling_working_set(steps, 0, q, eta) == sorted(set(case["first_support"]) | {0, q})
+    assert impl.rolling_working_set(steps, 2, q, eta) == sorted(set(case["first_support"]) | {2, 4, 5, 0, q})
+    assert impl.rolling_working_set(steps[1:], 1, q, eta) == case["union"]
+    # t = 4: the window is steps 1..4 (four steps), so the first step drops out
+    five = steps + steps[1:]
+    assert impl.rolling_working_set(five, 4, q, eta) == case["union"]
+    a = [[0, 1, 2, 5], [0, 3]]
+    b = [[0, 2], [0, 3]]
+    assert abs(impl.jaccard(a, b) - 4 / 6) < 1e-15
+    assert impl.jaccard(a, a) == 1.0
+    assert impl.jaccard([[1, 2]], [[3]]) == 0.0
+
+
 PINS = [pin_uniform_when_q_zero, pin_constant_values, pin_single_position,
         pin_logistic_two_keys, pin_causal_rows_sum_to_one, pin_key_shift_invariance,
         pin_scale_is_a_temperature, pin_golden_dense, pin_block_mass_sums_to_one,
@@ -389,7 +431,7 @@ PINS = [pin_uniform_when_q_zero, pin_constant_values, pin_single_position,
         pin_full_support_reproduces_dense, pin_diagonal_only_support,
         pin_sink_and_diagonal_support, pin_masked_rows_normalised,
         pin_variants_golden, pin_eta_support_brute_force, pin_union_structure,
-        pin_matched_controls]
+        pin_matched_controls, pin_retained_mass, pin_rolling_and_jaccard]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -583,7 +625,23 @@ def _mut_eta_support_exclusive(r, q, eta):
     return sorted(order[:k_star])
 
 
+def _mut_jaccard_per_row_mean(rows_a, rows_b):
+    vals = [len(set(a) & set(b)) / len(set(a) | set(b)) for a, b in zip(rows_a, rows_b)]
+    return float(np.mean(vals))
+
+
+def _mut_rolling_window_five(step_rows, t, q, eta):
+    return oracle.select_union(list(step_rows)[max(0, t - 4):t + 1], q, eta)
+
+
+def _mut_retained_counts_repeats(mass_row, support_row, q):
+    return float(sum(mass_row[b] for b in support_row if 0 <= b <= q))
+
+
 MUTANTS = {
+    "jaccard_per_row_mean": dict(jaccard=_mut_jaccard_per_row_mean),
+    "rolling_window_five_steps": dict(rolling_working_set=_mut_rolling_window_five),
+    "retained_counts_repeats": dict(retained_mass=_mut_retained_counts_repeats),
     "union_is_intersection": dict(select_union=_mut_union_is_intersection),
     "union_selects_on_mean": dict(select_union=_mut_union_of_mean),
     "static_wrong_step": dict(select_static=_mut_static_uses_last_step),
