@@ -296,6 +296,7 @@ def main(argv=None):
     # and the early-static controls with the first step; then the late
     # sparse launch on each variant's support.
     variants = None
+    diagnostics = None
     if not args.no_variants:
         step_mass = torch.zeros(td, cfg.batch, cfg.heads, nb, nb, dtype=torch.float32, device=dev)
         for t in range(td):
@@ -325,7 +326,38 @@ def main(argv=None):
                               "steps": "union of steps %d..%d" % (td - min(4, td), td - 1) if name == "union"
                               else ("step 0" if name == "static" else
                                     "step 0 ranking; union of steps %d..%d" % (td - min(4, td), td - 1))}
-        del step_mass, win, first, ctrl
+        # Diagnostics (Section 7; Appendix C.2): unrestricted block masses
+        # at the late steps too, then the retained future attention mass of
+        # the frozen supports, the adjacent rolling-set Jaccard at the
+        # switch (Eq. 24) and the switch-vs-final Jaccard (Eq. 25).
+        late_mass = torch.zeros(T - td, cfg.batch, cfg.heads, nb, nb, dtype=torch.float32, device=dev)
+        for t in range(td, T):
+            wise.wise_full_attn_accum(qs[t], ks[t], vs[t], late_mass[t - td], B, o=outs[t])
+        sel_union = wise.wise_select_variant(wise.SELECT_UNION, win, cfg.eta, D, B)
+
+        def retained(csr):
+            vals = [wise.wise_support_mass(late_mass[i], csr[0], csr[1], D, B) for i in range(T - td)]
+            return float(torch.stack(vals).double().mean().item())
+
+        def jacc(a, bb):
+            inter, uni = wise.wise_support_overlap(a, bb, cfg.batch, cfg.heads, nb, D, B)
+            per_b = inter.view(cfg.batch, -1).double().sum(1) / uni.view(cfg.batch, -1).double().sum(1)
+            return float(per_b.mean().item())
+        w = min(4, td)
+        prev = step_mass[max(0, td - 1 - w):td - 1].contiguous() if td >= 2 else win
+        fin = late_mass[T - td - min(4, T - td):].contiguous()
+        w_prev = wise.wise_select_variant(wise.SELECT_UNION, prev, cfg.eta, D, B)
+        w_fin = wise.wise_select_variant(wise.SELECT_UNION, fin, cfg.eta, D, B)
+        diagnostics = {
+            "retained_future_mass": round(retained((row_ptr, col_idx)), 4),
+            "retained_future_mass_union": round(retained(sel_union), 4),
+            "rolling_jaccard_at_switch": round(jacc(sel_union, w_prev), 4),
+            "jaccard_switch_vs_final": round(jacc(sel_union, w_fin), 4),
+            "note": (f"unrestricted masses of late steps {td}..{T - 1}; frozen supports: the main selection "
+                     f"and the union of steps {td - w}..{td - 1}; rolling sets of Eq. 23 at steps "
+                     f"{td - 2} and {T - 1}"),
+        }
+        del step_mass, win, first, ctrl, late_mass
     k4_ms = med(per["k4"]) / n_late            # one sparse launch
     k1_ms = med(per["k1"]) / td                # one discovery launch (incl. the mass memset share)
     k3_ms = med(per["k3"])
@@ -383,6 +415,8 @@ def main(argv=None):
         for vv in variants.values():
             vv["late_step_speedup_vs_dense"] = round(k2 / vv["sparse_ms"], 3)
         result["selection_variants"] = variants
+    if diagnostics is not None:
+        result["diagnostics"] = diagnostics
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a sample (cpu_baseline)")
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_heads)
