@@ -147,14 +147,16 @@ __host__ __device__ constexpr bool uses_dma() { return MODE != kDenseMass; }
 // that four waves share every staged K/V tile (the two rows' key-block
 // lists overlap heavily), one row otherwise.  The mass mode keeps one row
 // when the per-(query, key block) partials of two rows would not fit.
-template <int D, int BLK, int KT, int RPW>
+// nblk: physical blocks of BLK keys; LPR logical blocks of BLK/LPR keys per
+// physical block (LPR = 2 runs block 16 on 32 x 32 tiles).
+template <int D, int BLK, int KT, int RPW, int LPR = 1>
 __host__ __device__ constexpr size_t attn_lds_need(int mode, int nblk) {
   return (mode != kDenseMass ? (size_t)DmaTile<D, KT, AttnShape<D, BLK, KT, RPW>::kThreads>::kStages *
                                    DmaTile<D, KT, AttnShape<D, BLK, KT, RPW>::kThreads>::kStageBytes
                              : AttnShape<D, BLK, KT, RPW>::kTileLds) +
-         (mode == kDenseMass ? (size_t)RPW * ((size_t)nblk * (BLK + 1) + BLK) * 4 : 0) +
-         (mode == kMassTwoPass ? (size_t)RPW * nblk * (BLK / 32) * 4 : 0) +
-         (mode == kSparse ? (size_t)RPW * ((nblk + 31) / 32) * 4 + ((size_t)nblk + 1) * 4 : 0);
+         (mode == kDenseMass ? (size_t)RPW * ((size_t)nblk * LPR * (BLK + 1) + BLK) * 4 : 0) +
+         (mode == kMassTwoPass ? (size_t)RPW * LPR * nblk * LPR * (BLK / 32) * 4 : 0) +
+         (mode == kSparse ? (size_t)RPW * LPR * ((nblk * LPR + 31) / 32) * 4 + ((size_t)nblk + 1) * 4 : 0);
 }
 
 template <int D, int BLK, int KT, int RPW>
@@ -236,11 +238,18 @@ __device__ __forceinline__ void softmax_prep(float* part, float scale_log2, int 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-template <int D, int BLK, int KT, int MODE, int RPW>
+// LPR = 2: block 16 run on 32-query x 32-key physical tiles.  Each physical
+// row holds logical query blocks 2q and 2q+1 (queries 0-15 and 16-31 of the
+// wave), each physical key tile logical key blocks 2kb and 2kb+1 (a lane's
+// score values 0-7 and 8-15); CSR rows, masses and the sparse masks are per
+// logical block.
+template <int D, int BLK, int KT, int MODE, int RPW, int LPR = 1>
 __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(AttnParams p) {
   using Sh = AttnShape<D, BLK, KT, RPW>;
-  using St = AttnShape<D, BLK, KT>;
   constexpr int WR = BLK / 32;                 // waves per row
+  constexpr int kLB = BLK / LPR;               // logical block size
+  static_assert(LPR == 1 || (LPR == 2 && BLK == 32 && KT == 32 && RPW == 1 && MODE != kDense),
+                "logical sub-blocks: block 16 on 32 x 32 tiles, one row per workgroup");
 
   using Dm = DmaTile<D, KT, Sh::kThreads>;
   constexpr bool kDma = uses_dma<MODE>();
@@ -250,9 +259,10 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);
   uint16_t* Vs = Ks + KT * Sh::kKsStride;
   unsigned char* extra = smem + (kDma ? (size_t)Dm::kStages * Dm::kStageBytes : Sh::kTileLds);
-  const int nwords = (p.nblk + 31) / 32;
-  uint32_t* bits = reinterpret_cast<uint32_t*>(extra);                  // kSparse: [RPW][nwords]
-  int32_t* ulist = reinterpret_cast<int32_t*>(bits + RPW * nwords);     // kSparse: [nblk + 1]
+  const int lnb = p.nblk * LPR;                 // logical blocks per head
+  const int nwords = (lnb + 31) / 32;
+  uint32_t* bits = reinterpret_cast<uint32_t*>(extra);                  // kSparse: [RPW*LPR][nwords]
+  int32_t* ulist = reinterpret_cast<int32_t*>(bits + RPW * LPR * nwords);   // kSparse: [nblk + 1]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -292,9 +302,9 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   const bool row_ok = qb < p.nblk;
   const int row = bh * p.nblk + qb;
 
-  float* part = reinterpret_cast<float*>(extra) + (size_t)slot * ((size_t)p.nblk * (BLK + 1) + BLK);
-  float* invl = part + (size_t)p.nblk * (BLK + 1);                        // kDenseMass
-  float* slots = reinterpret_cast<float*>(extra);   // kMassTwoPass: [RPW][nblk][BLK/32]
+  float* part = reinterpret_cast<float*>(extra) + (size_t)slot * ((size_t)lnb * (BLK + 1) + BLK);
+  float* invl = part + (size_t)lnb * (BLK + 1);                           // kDenseMass
+  float* slots = reinterpret_cast<float*>(extra);   // kMassTwoPass: [RPW*LPR][lnb][BLK/32]
 
   const size_t head_off = (size_t)bh * p.seq * D;
   // grouped-query attention: query head h of batch entry b reads K/V head h / kv_group
@@ -364,7 +374,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   // starts elsewhere.
   if constexpr (MODE == kMassTwoPass) {
     dma_k(0, 0);
-    for (int i = tid; i < RPW * p.nblk * WR; i += Sh::kThreads) slots[i] = 0.f;
+    for (int i = tid; i < RPW * LPR * lnb * WR; i += Sh::kThreads) slots[i] = 0.f;
   } else if constexpr (kDma) {
     dma_tile(0, 0);
   }
@@ -376,26 +386,37 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   // order does not matter), then wave 0 compacts the union with ballots.
   int n_ent = q_hi + 1;
   if constexpr (MODE == kSparse) {
-    for (int i = tid; i < RPW * nwords; i += Sh::kThreads) bits[i] = 0u;
+    for (int i = tid; i < RPW * LPR * nwords; i += Sh::kThreads) bits[i] = 0u;
     lds_barrier();
     if (wr == 0 && row_ok) {
-      int e_begin = p.row_ptr[row];
-      int e_end = p.row_ptr[row + 1];
-      if (e_end < e_begin) e_end = e_begin;
-      for (int idx = e_begin + lane; idx < e_end; idx += 64) {
-        const int c = p.col_idx[idx];
-        if (c >= 0 && c <= qb) atomicOr(&bits[slot * nwords + (c >> 5)], 1u << (c & 31));
+#pragma unroll
+      for (int lr = 0; lr < LPR; ++lr) {
+        const int lrow = row * LPR + lr, lq = qb * LPR + lr;   // logical row and query block
+        int e_begin = p.row_ptr[lrow];
+        int e_end = p.row_ptr[lrow + 1];
+        if (e_end < e_begin) e_end = e_begin;
+        uint32_t* rb = bits + (slot * LPR + lr) * nwords;
+        for (int idx = e_begin + lane; idx < e_end; idx += 64) {
+          const int c = p.col_idx[idx];
+          if (c >= 0 && c <= lq) atomicOr(&rb[c >> 5], 1u << (c & 31));
+        }
       }
     }
     lds_barrier();
     if (wave == 0) {
+      // tag bit 28 + (row slot * LPR + logical row) * LPR + logical key half
       int count = 0;
       for (int base = 0; base <= q_hi; base += 64) {
         const int c = base + lane;
         uint32_t tag = 0;
         if (c <= q_hi) {
 #pragma unroll
-          for (int r = 0; r < RPW; ++r) tag |= ((bits[r * nwords + (c >> 5)] >> (c & 31)) & 1u) << (29 + r);
+          for (int r = 0; r < RPW * LPR; ++r)
+#pragma unroll
+            for (int kh = 0; kh < LPR; ++kh) {
+              const int lc = c * LPR + kh;
+              tag |= ((bits[r * nwords + (lc >> 5)] >> (lc & 31)) & 1u) << (28 + r * LPR + kh);
+            }
         }
         const uint64_t bal = __ballot(tag != 0);
         if (tag != 0) ulist[1 + count + __popcll(bal & ((1ull << lane) - 1ull))] = (int)(tag | (uint32_t)c);
@@ -406,16 +427,24 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
     lds_barrier();
     n_ent = __builtin_amdgcn_readfirstlane(ulist[0]);
   }
-  // Entry e -> (key block, does this wave's row list it).
-  auto entry = [&](int e, int& kb, bool& mine) {
+  // Entry e -> (key block, does this wave's row list it, and for LPR = 2
+  // which (logical query block, logical key block) pairs it lists: bit
+  // 2*lr + kh).
+  auto entry3 = [&](int e, int& kb, bool& mine, uint32_t& pairs) {
     if constexpr (MODE == kSparse) {
       const uint32_t code = (uint32_t)__builtin_amdgcn_readfirstlane(ulist[1 + e]);
-      kb = (int)(code & 0x1FFFFFFFu);
-      mine = row_ok && ((code >> (29 + slot)) & 1u);
+      kb = (int)(code & 0x0FFFFFFFu);
+      pairs = (code >> (28 + slot * LPR * LPR)) & ((1u << (LPR * LPR)) - 1u);
+      mine = row_ok && pairs != 0;
     } else {
       kb = e;
       mine = row_ok && e <= qb;
+      pairs = (1u << (LPR * LPR)) - 1u;
     }
+  };
+  auto entry = [&](int e, int& kb, bool& mine) {
+    uint32_t pairs;
+    entry3(e, kb, mine, pairs);
   };
   const int n_tiles = n_ent * Sh::kSub;
 
@@ -478,8 +507,8 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
 
   // Causal mask (diagonal block only), lazy-rescale check and rare rescale.
   auto prep = [&]<bool MASKED>(int kb, int sub, f32x16_t (&sc)[Sh::kM]) __attribute__((always_inline)) {
-    softmax_prep<D, BLK, KT, MODE, MASKED>(part, p.scale_log2, qrow - (kb * BLK + sub * KT), g, n, wr, kb,
-                                           m_ref, l_part, blk_part, sc, oacc);
+    softmax_prep<D, BLK, KT, MODE, MASKED>(part, p.scale_log2, qrow - (kb * BLK + sub * KT), g, n, wr,
+                                           kb * LPR, m_ref, l_part, blk_part, sc, oacc);
   };
 
   // P = exp2(s * scale*log2e - m) per 32-key sub-tile, then that
@@ -489,6 +518,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   auto expv = [&](int kb, int sub, f32x16_t (&sc)[Sh::kM], const uint16_t* Vt) __attribute__((always_inline)) {
     const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
     float tsum = 0.f;
+    float hsum[2] = {0.f, 0.f};   // LPR = 2 mass: per logical key half
 #pragma unroll
     for (int m = 0; m < Sh::kM; ++m) {
       bf16x8_t pf[2];
@@ -498,6 +528,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
         for (int e = 0; e < 8; ++e) {
           const float pv = __builtin_amdgcn_exp2f(fmaf(sc[m][kk * 8 + e], p.scale_log2, neg_m));
           if constexpr (MODE == kDenseMass) tsum += pv;   // block mass needs the fp32 values
+          if constexpr (MODE == kDenseMass && LPR == 2) hsum[kk] += pv;
           pf[kk][e] = (__bf16)pv;
         }
       if constexpr (MODE != kDenseMass) {
@@ -531,7 +562,13 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
     }
     __builtin_amdgcn_s_setprio(0);
     l_part += tsum;
-    if constexpr (MODE == kDenseMass) {
+    if constexpr (MODE == kDenseMass && LPR == 2) {
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const float bp = hsum[kh] + __shfl_xor(hsum[kh], 32);
+        if (g == 0) part[(kb * 2 + kh) * (BLK + 1) + n] = bp;
+      }
+    } else if constexpr (MODE == kDenseMass) {
       blk_part += tsum;
       if (sub == Sh::kSub - 1) {
         const float bp = blk_part + __shfl_xor(blk_part, 32);
@@ -545,12 +582,20 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   // The MFMA stretches run at raised wave priority: when both waves of a
   // SIMD are ready, the one feeding the matrix core issues first and the
   // other's softmax work fills the MFMA shadow.
-  auto compute_tile = [&]<bool MASKED>(int kb, int sub, const uint16_t* Kt,
-                                       const uint16_t* Vt) __attribute__((always_inline)) {
+  auto compute_tile = [&]<bool MASKED>(int kb, int sub, const uint16_t* Kt, const uint16_t* Vt,
+                                       uint32_t pairs) __attribute__((always_inline)) {
     f32x16_t sc[Sh::kM];
     __builtin_amdgcn_s_setprio(1);
     scores(sc, Kt);
     __builtin_amdgcn_s_setprio(0);
+    if constexpr (LPR == 2 && MODE == kSparse) {
+      // logical pairs this tile does not list: query half n/16, key half i/8
+      if (pairs != 0xFu) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (!((pairs >> (2 * (n >> 4) + (i >> 3))) & 1u)) sc[0][i] = -INFINITY;
+      }
+    }
     prep.template operator()<MASKED>(kb, sub, sc);
     expv(kb, sub, sc, Vt);
   };
@@ -587,6 +632,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
         }
     }
     float tsum = 0.f;
+    float hs[2] = {0.f, 0.f};     // LPR = 2: per logical key half
 #pragma unroll
     for (int m = 0; m < Sh::kM; ++m) {
       bf16x8_t pf[2];
@@ -596,6 +642,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
         for (int e = 0; e < 8; ++e) {
           const float pv = __builtin_amdgcn_exp2f(fmaf(sc[m][kk * 8 + e], p.scale_log2, neg_m)) * inv_l;
           tsum += pv;
+          if constexpr (LPR == 2) hs[kk] += pv;
           pf[kk][e] = (__bf16)pv;
         }
 #pragma unroll
@@ -612,10 +659,22 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
           oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], oacc[t], 0, 0, 0);
         }
     }
-    // sum over the wave's 32 queries x 2 key halves, fixed butterfly order
+    if constexpr (LPR == 1) {
+      // sum over the wave's 32 queries x 2 lane halves, fixed butterfly order
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) tsum += __shfl_xor(tsum, off);
-    if (lane == 0) slots[(slot * p.nblk + kb) * WR + wr] += tsum;
+      for (int off = 32; off >= 1; off >>= 1) tsum += __shfl_xor(tsum, off);
+      if (lane == 0) slots[(slot * lnb + kb) * WR + wr] += tsum;
+    } else {
+      // per (logical query block = query half, logical key block = key half)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        float v = hs[kh] + __shfl_xor(hs[kh], 32);
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+        if ((lane & 47) == 0)   // lanes 0 and 16
+          slots[((slot * LPR + (lane >> 4)) * lnb + kb * 2 + kh) * WR + wr] += v;
+      }
+    }
   };
 
   // Publish the prefetched tile, prefetch the next one, then every wave whose
@@ -669,7 +728,8 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
     for (int it = 0; it < n_tiles; ++it) {
       int kb;
       bool mine;
-      entry(it / Sh::kSub, kb, mine);
+      uint32_t pairs;
+      entry3(it / Sh::kSub, kb, mine, pairs);
       const int sub = it % Sh::kSub;
       const int st = it & 1;
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -678,8 +738,8 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
       const uint16_t* Kt = reinterpret_cast<const uint16_t*>(smem + st * Dm::kStageBytes);
       const uint16_t* Vt = Kt + KT * D;
       if (mine) {
-        if (kb == qb) compute_tile.template operator()<true>(kb, sub, Kt, Vt);
-        else compute_tile.template operator()<false>(kb, sub, Kt, Vt);
+        if (kb == qb) compute_tile.template operator()<true>(kb, sub, Kt, Vt, pairs);
+        else compute_tile.template operator()<false>(kb, sub, Kt, Vt, pairs);
       }
     }
   } else {
@@ -702,8 +762,8 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
       load_rows<D, BLK, KT, RPW>(vrs, nk, tid, vreg);
     }
     if (mine) {
-      if (kb == qb) compute_tile.template operator()<true>(kb, sub, Ks, Vs);
-      else compute_tile.template operator()<false>(kb, sub, Ks, Vs);
+      if (kb == qb) compute_tile.template operator()<true>(kb, sub, Ks, Vs, 0xFu);
+      else compute_tile.template operator()<false>(kb, sub, Ks, Vs, 0xFu);
     }
   }
   }
@@ -734,15 +794,17 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
 
   if constexpr (MODE == kMassTwoPass) {
     lds_barrier();
-    // r_qb = (1/B) * (sum of the row's wave slots, in wave order).
-    for (int w = tid; w < RPW * p.nblk; w += Sh::kThreads) {
-      const int r = w / p.nblk, b = w % p.nblk;
-      const int qr = q_lo + r;
-      if (qr >= p.nblk || b > qr) continue;
+    // r_qb = (1/B) * (sum of the logical row's wave slots, in wave order).
+    for (int w = tid; w < RPW * LPR * lnb; w += Sh::kThreads) {
+      const int rl = w / lnb, b = w % lnb;
+      const int qphys = q_lo + rl / LPR;
+      if (qphys >= p.nblk) continue;
+      const int lq = qphys * LPR + rl % LPR;
+      if (b > lq) continue;
       float acc = 0.f;
 #pragma unroll
-      for (int i = 0; i < WR; ++i) acc += slots[(r * p.nblk + b) * WR + i];
-      p.mass[((size_t)bh * p.nblk + qr) * p.nblk + b] += acc * (1.0f / BLK);
+      for (int i = 0; i < WR; ++i) acc += slots[(rl * lnb + b) * WR + i];
+      p.mass[((size_t)bh * lnb + lq) * lnb + b] += acc * (1.0f / kLB);
     }
   }
   if constexpr (MODE == kDenseMass) {
@@ -750,16 +812,19 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
     __syncthreads();
     // Row slot r's masses: r_qb = (1/B) sum_i partial_ib / l_i, one
     // sequential sum per key block (deterministic).
-    for (int w = tid; w < RPW * p.nblk; w += Sh::kThreads) {
-      const int r = w / p.nblk, b = w % p.nblk;
+    for (int w = tid; w < RPW * LPR * lnb; w += Sh::kThreads) {
+      const int rl = w / lnb, b = w % lnb;
+      const int r = rl / LPR, lr = rl % LPR;
       const int qr = q_lo + r;
-      if (qr >= p.nblk || b > qr) continue;
-      const float* pr = reinterpret_cast<float*>(extra) + (size_t)r * ((size_t)p.nblk * (BLK + 1) + BLK);
-      const float* il = pr + (size_t)p.nblk * (BLK + 1);
+      if (qr >= p.nblk) continue;
+      const int lq = qr * LPR + lr;
+      if (b > lq) continue;
+      const float* pr = reinterpret_cast<float*>(extra) + (size_t)r * ((size_t)lnb * (BLK + 1) + BLK);
+      const float* il = pr + (size_t)lnb * (BLK + 1);
       pr += b * (BLK + 1);
       float acc = 0.f;
-      for (int i = 0; i < BLK; ++i) acc = fmaf(pr[i], il[i], acc);
-      p.mass[((size_t)bh * p.nblk + qr) * p.nblk + b] += acc * (1.0f / BLK);
+      for (int i = lr * kLB; i < (lr + 1) * kLB; ++i) acc = fmaf(pr[i], il[i], acc);
+      p.mass[((size_t)bh * lnb + lq) * lnb + b] += acc * (1.0f / kLB);
     }
   }
 }
@@ -782,11 +847,11 @@ inline int choose_head_chunk(int heads_total, int n_groups, int wgs_per_cu) {
   return (int)std::max(1L, std::min<long>(hc, hpx));
 }
 
-template <int D, int BLK, int KT, int MODE, int RPW>
+template <int D, int BLK, int KT, int MODE, int RPW, int LPR = 1>
 hipError_t launch_attn_t(const AttnParams& p_in, hipStream_t stream) {
   using Sh = AttnShape<D, BLK, KT, RPW>;
-  const size_t lds = attn_lds_need<D, BLK, KT, RPW>(MODE, p_in.nblk);
-  auto kern = wise_attn_kernel<D, BLK, KT, MODE, RPW>;
+  const size_t lds = attn_lds_need<D, BLK, KT, RPW, LPR>(MODE, p_in.nblk);
+  auto kern = wise_attn_kernel<D, BLK, KT, MODE, RPW, LPR>;
   // Once per process: allow the full LDS budget and read how many
   // workgroups fit one CU by registers alone (thread-safe static init).
   static const int regs_wgs = [&]() -> int {
@@ -876,9 +941,16 @@ int fused_mass_waves(int nblk) {
 // fewer than WISE_TWO_PASS_BELOW_WAVES resident waves per CU; then it runs
 // in two passes over the keys (row max and sum, then normalised P), which
 // needs only one fp32 per (row, key block, wave) of LDS.
+// The one-pass mass kernel with one 32-query wave per workgroup stages a
+// whole 32-key tile per lane in VGPRs; at head_dim 128 that spills, so those
+// launches always take the two-pass form.
+template <int D, int BLK>
+constexpr bool fused_mass_spills() { return D == 128 && BLK == 32; }
+
 template <int D, int BLK>
 int effective_mode(int mode, int nblk) {
   if (mode != kDenseMass) return mode;
+  if constexpr (fused_mass_spills<D, BLK>()) return kMassTwoPass;
   if (fused_mass_waves<D, BLK>(nblk) >= WISE_TWO_PASS_BELOW_WAVES) return kDenseMass;
   const AttnCfg c = choose_cfg<D, BLK>(kMassTwoPass, nblk);
   return c.kt != 0 ? kMassTwoPass : kDenseMass;
@@ -903,7 +975,8 @@ hipError_t launch_cfg(AttnCfg c, const AttnParams& p, hipStream_t stream) {
       if (c.kt == 64) return launch_attn_t<D, 128, 64, MODE, 1>(p, stream);
       return launch_attn_t<D, 128, 32, MODE, 1>(p, stream);
     } else {
-      return launch_attn_t<D, 32, 32, MODE, 1>(p, stream);
+      if constexpr (fused_mass_spills<D, 32>()) return hipErrorInvalidValue;
+      else return launch_attn_t<D, 32, 32, MODE, 1>(p, stream);
     }
   }
 }
@@ -921,6 +994,41 @@ hipError_t launch_attn_blk(int mode_in, const AttnParams& p, hipStream_t stream)
   }
 }
 
+// Block 16: 32 x 32 physical tiles, two logical blocks per physical block
+// (nblk16 logical blocks, even).  The dense baseline does not depend on the
+// block size and runs the block-32 launch; the mass mode runs one pass when
+// its partials leave at least 4 resident waves per CU, else two passes.
+template <int D>
+int b16_mode(int mode, int nblk16) {
+  if (mode != kDenseMass) return mode;
+  if constexpr (fused_mass_spills<D, 32>()) return kMassTwoPass;
+  const size_t lds = attn_lds_need<D, 32, 32, 1, 2>(kDenseMass, nblk16 / 2);
+  const int waves = lds <= kMaxLds ? std::min((int)(kMaxLds / lds), 8) : 0;
+  return waves >= WISE_TWO_PASS_BELOW_WAVES ? kDenseMass : kMassTwoPass;
+}
+
+template <int D>
+size_t attn_lds_bytes_b16(int mode, int nblk16) {
+  if (nblk16 % 2 != 0) return 0;
+  if (mode == kDense) return attn_lds_need<D, 32, 32, 1>(kDense, nblk16 / 2);
+  return attn_lds_need<D, 32, 32, 1, 2>(b16_mode<D>(mode, nblk16), nblk16 / 2);
+}
+
+template <int D>
+hipError_t launch_attn_b16(int mode, const AttnParams& p16, hipStream_t stream) {
+  if (p16.nblk % 2 != 0) return hipErrorInvalidValue;
+  AttnParams p = p16;
+  p.nblk = p16.nblk / 2;     // physical 32-key blocks
+  switch (mode == kDense ? kDense : b16_mode<D>(mode, p16.nblk)) {
+    case kDense: return launch_attn_t<D, 32, 32, kDense, 1>(p, stream);
+    case kSparse: return launch_attn_t<D, 32, 32, kSparse, 1, 2>(p, stream);
+    case kMassTwoPass: return launch_attn_t<D, 32, 32, kMassTwoPass, 1, 2>(p, stream);
+    default:
+      if constexpr (fused_mass_spills<D, 32>()) return hipErrorInvalidValue;
+      else return launch_attn_t<D, 32, 32, kDenseMass, 1, 2>(p, stream);
+  }
+}
+
 template <int D, int BLK>
 size_t attn_lds_bytes_blk(int mode_in, int nblk) {
   const int mode = effective_mode<D, BLK>(mode_in, nblk);
@@ -931,6 +1039,7 @@ size_t attn_lds_bytes_blk(int mode_in, int nblk) {
 template <int D>
 size_t attn_lds_bytes_d(int block, int mode, int nblk) {
   switch (block) {
+    case 16: return attn_lds_bytes_b16<D>(mode, nblk);
     case 32: return attn_lds_bytes_blk<D, 32>(mode, nblk);
     case 64: return attn_lds_bytes_blk<D, 64>(mode, nblk);
     case 128: return attn_lds_bytes_blk<D, 128>(mode, nblk);
@@ -941,6 +1050,7 @@ size_t attn_lds_bytes_d(int block, int mode, int nblk) {
 template <int D>
 hipError_t launch_attn_d(int block, int mode, const AttnParams& p, hipStream_t stream) {
   switch (block) {
+    case 16: return launch_attn_b16<D>(mode, p, stream);
     case 32: return launch_attn_blk<D, 32>(mode, p, stream);
     case 64: return launch_attn_blk<D, 64>(mode, p, stream);
     case 128: return launch_attn_blk<D, 128>(mode, p, stream);

@@ -58,8 +58,8 @@ wise_status_t check_desc(const wise_attn_desc_t* d, int32_t* nblk, int64_t* n_ro
   if (d == nullptr) return fail(WISE_ERR_INVALID_ARG, "desc is NULL");
   if (d->batch < 1 || d->heads < 1)
     return fail(WISE_ERR_INVALID_ARG, "batch (%d) and heads (%d) must be >= 1", d->batch, d->heads);
-  if (d->block_size != 32 && d->block_size != 64 && d->block_size != 128)
-    return fail(WISE_ERR_UNSUPPORTED, "block_size %d not built (32, 64, 128)", d->block_size);
+  if (d->block_size != 16 && d->block_size != 32 && d->block_size != 64 && d->block_size != 128)
+    return fail(WISE_ERR_UNSUPPORTED, "block_size %d not built (16, 32, 64, 128)", d->block_size);
   if (d->head_dim != 64 && d->head_dim != 96 && d->head_dim != 128)
     return fail(WISE_ERR_UNSUPPORTED, "head_dim %d not built (64, 96, 128)", d->head_dim);
   if (d->seq_len < d->block_size || d->seq_len % d->block_size != 0)
@@ -110,6 +110,9 @@ wise_status_t run_attn(const wise_attn_desc_t* d, int mode, const void* q, const
     return fail(WISE_ERR_INVALID_ARG, "lse is not 4-byte aligned");
   if (mass != nullptr && (reinterpret_cast<uintptr_t>(mass) & 3u))
     return fail(WISE_ERR_INVALID_ARG, "mass is not 4-byte aligned");
+  if (d->block_size == 16 && d->seq_len % 32 != 0)
+    return fail(WISE_ERR_UNSUPPORTED, "block_size 16 attention needs seq_len %d to be a multiple of 32",
+                d->seq_len);
   const size_t lds = attn_lds_bytes(d->head_dim, d->block_size, mode, nblk);
   if (lds == 0 || lds > kMaxLds)
     return fail(WISE_ERR_UNSUPPORTED, "seq_len %d needs %zu B of LDS for this call", d->seq_len, lds);

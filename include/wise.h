@@ -65,7 +65,9 @@ typedef struct {
   int32_t heads;       /* >= 1 query heads (Q, O, mass and CSR rows)   */
   int32_t seq_len;     /* >= block_size, multiple of block_size         */
   int32_t head_dim;    /* 64, 96 or 128                                 */
-  int32_t block_size;  /* B of Section 5.1: 32, 64 or 128               */
+  int32_t block_size;  /* B of Section 5.1: 16, 32, 64 or 128 (16: the
+                          attention calls need seq_len % 32 == 0; they run
+                          two 16-blocks per 32 x 32 tile)                */
   float softmax_scale; /* <= 0 selects 1/sqrt(head_dim)                 */
   int32_t kv_heads;    /* K/V heads: 0 (= heads) or a divisor of heads;
                           query head h reads K/V head h / (heads / kv_heads)

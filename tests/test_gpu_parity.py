@@ -28,6 +28,9 @@ def _need_gpu():
 
 # (batch, heads, seq, head_dim, block): small shapes covering every built kernel.
 SHAPES = [
+    (1, 2, 256, 64, 16),      # block 16: two logical blocks per 32 x 32 tile
+    (2, 1, 160, 128, 16),     # 10 logical blocks; the mass runs in two passes
+    (1, 2, 192, 96, 16),
     (1, 2, 256, 64, 32),
     (2, 1, 160, 96, 32),      # 5 blocks
     (1, 2, 320, 128, 64),     # 5 blocks
@@ -105,7 +108,7 @@ def test_dense_large_logits_rescale_path(d_, blk):
         assert np.max(np.abs(mass_h[0, h] - np.tril(r))) < 1e-3
 
 
-@pytest.mark.parametrize("shape", SHAPES[:6], ids=[f"b{s[0]}h{s[1]}s{s[2]}d{s[3]}B{s[4]}" for s in SHAPES[:6]])
+@pytest.mark.parametrize("shape", SHAPES[:9], ids=[f"b{s[0]}h{s[1]}s{s[2]}d{s[3]}B{s[4]}" for s in SHAPES[:9]])
 def test_accum_mass_matches_oracle(shape):
     b_, h_, s_, d_, blk = shape
     say(f"accum {shape}")
@@ -263,8 +266,8 @@ def test_sparse_empty_rows_give_zeros():
     compare_outputs(got, ref, "sparse O with empty rows")
 
 
-@pytest.mark.parametrize("shape", [SHAPES[0], SHAPES[2], SHAPES[5], SHAPES[3]],
-                         ids=["d64B32", "d128B64", "d128B128", "d96B64b2"])
+@pytest.mark.parametrize("shape", [SHAPES[3], SHAPES[5], SHAPES[8], SHAPES[6], SHAPES[0], SHAPES[1]],
+                         ids=["d64B32", "d128B64", "d128B128", "d96B64b2", "d64B16", "d128B16b2"])
 def test_sparse_full_support_equals_dense_bitwise(shape):
     """Same backend on every causal block: the sparse kernel reproduces the
     dense kernel exactly (same tiles in the same order)."""
@@ -280,7 +283,7 @@ def test_sparse_full_support_equals_dense_bitwise(shape):
 
 
 def test_deterministic_repeat():
-    shape = SHAPES[2]
+    shape = SHAPES[5]
     b_, h_, s_, d_, blk = shape
     _, q, k, v = _steps(_cfg(*shape), 1)[0]
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
@@ -324,7 +327,8 @@ def test_small_trajectories_end_to_end():
     """Scaled-down versions of the 4K, wide-head and long-context workloads."""
     for cfg in (CONFIGS["ctx4k"].with_(heads=2, seq_len=1024, steps=6, td=3),
                 CONFIGS["wide"].with_(batch=2, heads=3, seq_len=768, steps=5, td=2),
-                CONFIGS["long"].with_(heads=2, seq_len=2048, steps=4, td=2, cap=6)):
+                CONFIGS["long"].with_(heads=2, seq_len=2048, steps=4, td=2, cap=6),
+                CONFIGS["ctx4k"].with_(heads=2, seq_len=1024, block=16, steps=5, td=2, index=77)):
         say(f"trajectory {cfg.name} {cfg.batch}x{cfg.heads} S{cfg.seq_len}")
         steps = _steps(cfg)
         mass, row_ptr, col_idx, outs = run_trajectory(cfg, steps)
