@@ -44,6 +44,8 @@ def parse(argv=None):
     ap.add_argument("--cpu-heads", type=int, default=4)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB first (HBM counter calibration)")
+    ap.add_argument("--no-block-study", action="store_true",
+                    help="skip the block-size study (the same inputs at block 16, 32, 64, 128)")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the selection-variant figures (temporal union and the early-static controls)")
     ap.add_argument("--same-backend", action="store_true",
@@ -410,6 +412,36 @@ def main(argv=None):
                      "compulsory_GBps": round(sparse_bytes(cfg, fc["nnz"], fc["n_rows"]) /
                                               (k4_ms * 1e-3) / 1e9, 1)},
     }
+    # Block-size study (the pages' B in {16, 32, 64, 128} ablation): the
+    # same inputs, discovery masses, selection and late sparse launches at
+    # every block size; the dense denominator is the workload's own dense
+    # launch (its cost does not depend on the block size).
+    block_study = None
+    if not args.no_block_study:
+        block_study = {}
+        k2_ms_ref = med(dts) / n_late
+        for Bs in (16, 32, 64, 128):
+            if cfg.seq_len % max(Bs, 32) != 0:
+                continue
+            cfg_b = cfg.with_(block=Bs)
+            nb_b = cfg.seq_len // Bs
+            m_b = torch.zeros(cfg.batch, cfg.heads, nb_b, nb_b, dtype=torch.float32, device=dev)
+            for t in range(td):
+                wise.wise_full_attn_accum(qs[t], ks[t], vs[t], m_b, Bs, o=outs[t])
+            rp_b, ci_b = wise.wise_select_support(m_b, td, cfg.eta, D, Bs, cfg.cap)
+            fcb = flop_counts(cfg_b, rp_b.cpu().numpy())
+
+            def late_b():
+                for t in range(td, T):
+                    wise.wise_sparse_attn(qs[t], ks[t], vs[t], rp_b, ci_b, Bs, o=outs[t])
+            sp = timed_ms(late_b, 3) / n_late
+            block_study[str(Bs)] = {"density_admissible": round(fcb["density_adm"], 4),
+                                    "sparse_ms": round(sp, 4),
+                                    "sparse_tflops_exec": round(fcb["sparse_exec"] / (sp * 1e-3) / 1e12, 2),
+                                    "late_step_speedup_vs_dense": round(k2_ms_ref / sp, 3),
+                                    "ideal_speedup_1_over_density": round(1.0 / fcb["density_adm"], 3)}
+            del m_b, rp_b, ci_b
+
     if variants is not None:
         k2 = med(dts) / n_late
         for vv in variants.values():
@@ -417,6 +449,8 @@ def main(argv=None):
         result["selection_variants"] = variants
     if diagnostics is not None:
         result["diagnostics"] = diagnostics
+    if block_study is not None:
+        result["block_size_study"] = block_study
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a sample (cpu_baseline)")
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_heads)
