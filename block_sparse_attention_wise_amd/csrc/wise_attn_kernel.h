@@ -248,8 +248,9 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   using Sh = AttnShape<D, BLK, KT, RPW>;
   constexpr int WR = BLK / 32;                 // waves per row
   constexpr int kLB = BLK / LPR;               // logical block size
-  static_assert(LPR == 1 || (LPR == 2 && BLK == 32 && KT == 32 && RPW == 1 && MODE != kDense),
-                "logical sub-blocks: block 16 on 32 x 32 tiles, one row per workgroup");
+  static_assert(LPR == 1 || (LPR == 2 && BLK == 32 && KT == 32 && RPW <= 2 && MODE != kDense),
+                "logical sub-blocks: block 16 on 32 x 32 tiles, at most two rows per workgroup");
+  static_assert(RPW * LPR * LPR <= 8, "list-entry tag bits");
 
   using Dm = DmaTile<D, KT, Sh::kThreads>;
   constexpr bool kDma = uses_dma<MODE>();
@@ -404,7 +405,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
     }
     lds_barrier();
     if (wave == 0) {
-      // tag bit 28 + (row slot * LPR + logical row) * LPR + logical key half
+      // tag bit 24 + (row slot * LPR + logical row) * LPR + logical key half
       int count = 0;
       for (int base = 0; base <= q_hi; base += 64) {
         const int c = base + lane;
@@ -415,7 +416,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
 #pragma unroll
             for (int kh = 0; kh < LPR; ++kh) {
               const int lc = c * LPR + kh;
-              tag |= ((bits[r * nwords + (lc >> 5)] >> (lc & 31)) & 1u) << (28 + r * LPR + kh);
+              tag |= ((bits[r * nwords + (lc >> 5)] >> (lc & 31)) & 1u) << (24 + r * LPR + kh);
             }
         }
         const uint64_t bal = __ballot(tag != 0);
@@ -433,8 +434,8 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   auto entry3 = [&](int e, int& kb, bool& mine, uint32_t& pairs) {
     if constexpr (MODE == kSparse) {
       const uint32_t code = (uint32_t)__builtin_amdgcn_readfirstlane(ulist[1 + e]);
-      kb = (int)(code & 0x0FFFFFFFu);
-      pairs = (code >> (28 + slot * LPR * LPR)) & ((1u << (LPR * LPR)) - 1u);
+      kb = (int)(code & 0x00FFFFFFu);
+      pairs = (code >> (24 + slot * LPR * LPR)) & ((1u << (LPR * LPR)) - 1u);
       mine = row_ok && pairs != 0;
     } else {
       kb = e;
@@ -886,6 +887,7 @@ size_t cfg_lds(int kt, int rpw, int mode, int nblk) {
   }
   if (kt == 32 && rpw == 1) return attn_lds_need<D, BLK, 32, 1>(mode, nblk);
   if (kt == 32 && rpw == 2) return attn_lds_need<D, BLK, 32, 2>(mode, nblk);
+  if (kt == 32 && rpw == 4) return attn_lds_need<D, BLK, 32, 4>(mode, nblk);
   return 0;
 }
 
@@ -893,15 +895,24 @@ size_t cfg_lds(int kt, int rpw, int mode, int nblk) {
 #define WISE_SPARSE_RPW64 2
 #endif
 
+// Rows per workgroup of the block-32 dense, sparse and two-pass launches:
+// one-wave rows, so several share every staged tile (four for the dense
+// walks, two for the sparse union walk; two at head_dim 96, whose 32-key
+// tile does not split into four waves' loads).
+template <int D, int MODE>
+constexpr int rpw32() { return (MODE == kSparse || D == 96) ? 2 : 4; }
+
 // Dense and sparse launches: 64-key tiles (32 for block 32), two rows per
-// workgroup for block 64.  Mass launches: the candidate with the most
+// workgroup for block 64, rpw32() rows for block 32.  Mass launches: the candidate with the most
 // resident waves per CU under the LDS budget (two 2-wave rows, or one row;
 // 64- or 32-key tiles), preferring two rows and larger tiles on ties.
 template <int D, int BLK>
 AttnCfg choose_cfg(int mode, int nblk) {
   constexpr int kWavesPerRow = BLK / 32;
   if (mode != kDenseMass) {
-    const AttnCfg c{BLK >= 64 ? 64 : 32, BLK == 64 ? (mode == kSparse ? WISE_SPARSE_RPW64 : 2) : 1};
+    const int r32 = mode == kSparse ? rpw32<D, kSparse>() : rpw32<D, kDense>();
+    const AttnCfg c{BLK >= 64 ? 64 : 32, BLK == 64 ? (mode == kSparse ? WISE_SPARSE_RPW64 : 2)
+                                                   : (BLK == 32 ? r32 : 1)};
     return cfg_lds<D, BLK>(c.kt, c.rpw, mode, nblk) <= kMaxLds ? c : AttnCfg{0, 0};
   }
   // (head_dim 128 at block 64 with 64-key tiles spills registers in this mode)
@@ -942,15 +953,20 @@ int fused_mass_waves(int nblk) {
 // in two passes over the keys (row max and sum, then normalised P), which
 // needs only one fp32 per (row, key block, wave) of LDS.
 // The one-pass mass kernel with one 32-query wave per workgroup stages a
-// whole 32-key tile per lane in VGPRs; at head_dim 128 that spills, so those
-// launches always take the two-pass form.
+// whole 32-key tile per lane in VGPRs; at head_dim 128 that spills.
 template <int D, int BLK>
 constexpr bool fused_mass_spills() { return D == 128 && BLK == 32; }
+
+// Block 32 mass launches always take the two-pass form: it runs rpw32()
+// one-wave rows per workgroup sharing every staged tile, the one-pass form
+// only one.
+template <int D, int BLK>
+constexpr bool two_pass_only() { return BLK == 32; }
 
 template <int D, int BLK>
 int effective_mode(int mode, int nblk) {
   if (mode != kDenseMass) return mode;
-  if constexpr (fused_mass_spills<D, BLK>()) return kMassTwoPass;
+  if constexpr (two_pass_only<D, BLK>()) return kMassTwoPass;
   if (fused_mass_waves<D, BLK>(nblk) >= WISE_TWO_PASS_BELOW_WAVES) return kDenseMass;
   const AttnCfg c = choose_cfg<D, BLK>(kMassTwoPass, nblk);
   return c.kt != 0 ? kMassTwoPass : kDenseMass;
@@ -961,7 +977,7 @@ hipError_t launch_cfg(AttnCfg c, const AttnParams& p, hipStream_t stream) {
   if constexpr (MODE != kDenseMass) {
     if constexpr (BLK == 64) return launch_attn_t<D, 64, 64, MODE, MODE == kSparse ? WISE_SPARSE_RPW64 : 2>(p, stream);
     else if constexpr (BLK == 128) return launch_attn_t<D, 128, 64, MODE, 1>(p, stream);
-    else return launch_attn_t<D, 32, 32, MODE, 1>(p, stream);
+    else return launch_attn_t<D, 32, 32, MODE, rpw32<D, MODE>()>(p, stream);
   } else {
     if constexpr (BLK == 64) {
       if constexpr (D != 128) {
@@ -975,8 +991,7 @@ hipError_t launch_cfg(AttnCfg c, const AttnParams& p, hipStream_t stream) {
       if (c.kt == 64) return launch_attn_t<D, 128, 64, MODE, 1>(p, stream);
       return launch_attn_t<D, 128, 32, MODE, 1>(p, stream);
     } else {
-      if constexpr (fused_mass_spills<D, 32>()) return hipErrorInvalidValue;
-      else return launch_attn_t<D, 32, 32, MODE, 1>(p, stream);
+      return hipErrorInvalidValue;   // block 32 mass launches are two-pass (effective_mode)
     }
   }
 }
@@ -1010,8 +1025,10 @@ int b16_mode(int mode, int nblk16) {
 template <int D>
 size_t attn_lds_bytes_b16(int mode, int nblk16) {
   if (nblk16 % 2 != 0) return 0;
-  if (mode == kDense) return attn_lds_need<D, 32, 32, 1>(kDense, nblk16 / 2);
-  return attn_lds_need<D, 32, 32, 1, 2>(b16_mode<D>(mode, nblk16), nblk16 / 2);
+  if (mode == kDense) return attn_lds_need<D, 32, 32, rpw32<D, kDense>()>(kDense, nblk16 / 2);
+  const int m = b16_mode<D>(mode, nblk16);
+  return m == kDenseMass ? attn_lds_need<D, 32, 32, 1, 2>(m, nblk16 / 2)
+                         : attn_lds_need<D, 32, 32, 2, 2>(m, nblk16 / 2);
 }
 
 template <int D>
@@ -1020,9 +1037,9 @@ hipError_t launch_attn_b16(int mode, const AttnParams& p16, hipStream_t stream) 
   AttnParams p = p16;
   p.nblk = p16.nblk / 2;     // physical 32-key blocks
   switch (mode == kDense ? kDense : b16_mode<D>(mode, p16.nblk)) {
-    case kDense: return launch_attn_t<D, 32, 32, kDense, 1>(p, stream);
-    case kSparse: return launch_attn_t<D, 32, 32, kSparse, 1, 2>(p, stream);
-    case kMassTwoPass: return launch_attn_t<D, 32, 32, kMassTwoPass, 1, 2>(p, stream);
+    case kDense: return launch_attn_t<D, 32, 32, kDense, rpw32<D, kDense>()>(p, stream);
+    case kSparse: return launch_attn_t<D, 32, 32, kSparse, 2, 2>(p, stream);
+    case kMassTwoPass: return launch_attn_t<D, 32, 32, kMassTwoPass, 2, 2>(p, stream);
     default:
       if constexpr (fused_mass_spills<D, 32>()) return hipErrorInvalidValue;
       else return launch_attn_t<D, 32, 32, kDenseMass, 1, 2>(p, stream);
