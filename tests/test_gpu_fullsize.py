@@ -89,3 +89,42 @@ def test_full_size_trajectory(name):
         lambda b, h: wl.head_steps(b, h, n_steps), out_steps=range(n_steps))
     say(f"  {stats['rows']} sampled rows, {stats['margin_rows']} near-margin supports, "
         f"max-abs {stats['max_abs']:.2e}, mean-abs {np.mean(stats['mean_abs']):.2e}")
+
+
+# Largest sizes the library accepts: 65536 keys (the descriptor limit), 2048
+# key blocks per row (the selection limit) at block 32 and at block 16.
+MAX_SHAPES = [(65536, 128, 64), (65536, 64, 32), (32768, 96, 16)]
+
+
+@pytest.mark.parametrize("shape", MAX_SHAPES, ids=[f"s{s[0]}d{s[1]}B{s[2]}" for s in MAX_SHAPES])
+def test_maximum_sizes(shape):
+    s_, d_, blk = shape
+    cfg = CONFIGS["tiny"].with_(batch=1, heads=1, seq_len=s_, head_dim=d_, block=blk, steps=3, td=2,
+                                planted=(8, 8), beta=2.0, sigma=0.02, index=900 + blk)
+    nb = cfg.n_blocks
+    rng = np.random.default_rng(cfg.seed)
+    qbs = sorted({0, 1, nb // 2, nb - 2, nb - 1} | set(int(x) for x in rng.integers(0, nb, 2)))
+    samples = [(0, 0, qb) for qb in qbs]
+    say(f"maximum size {shape}: {nb} blocks, sampled rows {qbs}")
+    mass = torch.zeros(1, 1, nb, nb, dtype=torch.float32, device="cuda")
+    got = {}
+    row_ptr = col_idx = None
+    for t, q, k, v in Workload(cfg, threads=16).steps():
+        qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+        if t < cfg.td:
+            o = wise.wise_full_attn_accum(qd, kd, vd, mass, blk)
+        else:
+            row_ptr, col_idx = wise.wise_select_support(mass, cfg.td, cfg.eta, d_, blk)
+            o = wise.wise_sparse_attn(qd, kd, vd, row_ptr, col_idx, blk)
+        for qb in qbs:
+            got[(t, qb)] = bf16_dev_to_f64(o[0, 0, qb * blk:(qb + 1) * blk])
+        del qd, kd, vd, o
+    torch.cuda.synchronize()
+    gm = mass.cpu().numpy()
+    np.testing.assert_allclose(gm.sum(axis=-1), cfg.td, atol=1e-3 * cfg.td)
+    rows = csr_rows(row_ptr.cpu().numpy(), col_idx.cpu().numpy())
+    assert all(r[0] == 0 and r[-1] == i for i, r in enumerate(rows))
+    wl = Workload(cfg, threads=4)
+    stats = check_trajectory_rows(cfg, gm, rows, lambda t, b, h, r: got[(t, int(r[0]) // blk)], samples,
+                                  lambda b, h: wl.head_steps(b, h, cfg.steps), out_steps=range(cfg.steps))
+    say(f"  {stats['rows']} rows, max-abs {stats['max_abs']:.2e}")
