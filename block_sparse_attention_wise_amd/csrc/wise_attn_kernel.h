@@ -27,6 +27,7 @@
 #pragma once
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "wise_internal.h"
@@ -835,12 +836,24 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
 // longest-first order over its heads keeps the tail short; above that,
 // chunks of about two slot-fills keep few heads' K/V per L2.  Needs
 // heads_total % 8 == 0 (each head then stays on one XCD).
-inline int choose_head_chunk(int heads_total, int n_groups, int wgs_per_cu) {
+constexpr int kMaxDevices = 64;
+
+// Compute units of device `dev`, cached per device (0 if unknown).
+inline int device_cus(int dev) {
+  static std::atomic<int> cache[kMaxDevices];   // zero: not read yet
+  if (dev < 0 || dev >= kMaxDevices) return 0;
+  int c = cache[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1) return 0;
+    cache[dev].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
+
+inline int choose_head_chunk(int dev, int heads_total, int n_groups, int wgs_per_cu) {
   if (heads_total % 8 != 0) return 0;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
-    return 0;
+  const int cus = device_cus(dev);
+  if (cus < 8) return 0;
   const int hpx = heads_total / 8;
   const long slots = (long)wgs_per_cu * (cus / 8);
   if ((long)hpx * n_groups <= 4 * slots) return hpx;
@@ -853,20 +866,27 @@ hipError_t launch_attn_t(const AttnParams& p_in, hipStream_t stream) {
   using Sh = AttnShape<D, BLK, KT, RPW>;
   const size_t lds = attn_lds_need<D, BLK, KT, RPW, LPR>(MODE, p_in.nblk);
   auto kern = wise_attn_kernel<D, BLK, KT, MODE, RPW, LPR>;
-  // Once per process: allow the full LDS budget and read how many
-  // workgroups fit one CU by registers alone (thread-safe static init).
-  static const int regs_wgs = [&]() -> int {
+  // Once per device: allow the full LDS budget and read how many
+  // workgroups fit one CU by registers alone.  Concurrent first calls may
+  // both do it; the attribute is idempotent and the value the same.
+  static std::atomic<int> ready[kMaxDevices];   // 0: not yet; else 1 + workgroups per CU
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  int rw = ready[dev].load(std::memory_order_acquire);
+  if (rw == 0) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds) != hipSuccess)
-      return -1;
+      return hipErrorInvalidDeviceFunction;
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, Sh::kThreads, 0) != hipSuccess) return -1;
-    return n;
-  }();
-  if (regs_wgs < 0) return hipErrorInvalidDeviceFunction;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, Sh::kThreads, 0) != hipSuccess)
+      return hipErrorInvalidDeviceFunction;
+    rw = 1 + n;
+    ready[dev].store(rw, std::memory_order_release);
+  }
+  const int regs_wgs = rw - 1;
   AttnParams p = p_in;
   const int n_groups = (p.nblk + RPW - 1) / RPW;
-  p.head_chunk = choose_head_chunk(p.heads_total, n_groups,
+  p.head_chunk = choose_head_chunk(dev, p.heads_total, n_groups,
                                    std::max(1, std::min(regs_wgs, (int)(kMaxLds / std::max<size_t>(lds, 1)))));
   const unsigned grid = (unsigned)p.heads_total * (unsigned)n_groups;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(Sh::kThreads), lds, stream, p);
