@@ -21,8 +21,9 @@
  * - Tensors are device pointers owned by the caller; the library allocates
  *   no device memory and keeps no state between calls.
  * - Q, K, V, O are bf16 (raw 16-bit patterns), contiguous, laid out
- *   [batch][heads][seq_len][head_dim].  Q, K and V are read-only; O may not
- *   alias them.  All pointers must be 16-byte aligned.
+ *   [batch][heads][seq_len][head_dim] (K and V: [batch][kv_heads][...]).
+ *   Q, K and V are read-only; O may not alias them.  All pointers must be
+ *   16-byte aligned.
  * - Attention is causal: key j is admissible for query i iff j <= i (the
  *   mask M of Eq. 2).  Scores are (q_i . k_j) * scale, scale = 1/sqrt(head_dim)
  *   unless desc->softmax_scale > 0.
@@ -37,8 +38,9 @@
  *   outputs (no atomics on any value path).
  * - No C++ exception crosses this interface.  The library is thread-safe.
  *
- * Supported shapes: head_dim in {64, 96, 128}; block_size in {32, 64, 128};
- * seq_len <= 65536; batch*heads*n_blocks < 2^31.
+ * Supported shapes: head_dim in {64, 96, 128}; block_size in {16, 32, 64,
+ * 128} (16: the attention calls need seq_len % 32 == 0); seq_len <= 65536;
+ * batch*heads*n_blocks < 2^31.
  */
 #ifndef WISE_H
 #define WISE_H
