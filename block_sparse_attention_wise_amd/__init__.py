@@ -8,7 +8,8 @@ there is no fallback path.  Build the library with
 ``python -m block_sparse_attention_wise_amd.build``.
 
 Layouts (see the header for the full contract):
-  q, k, v, o   bf16  [batch, heads, seq_len, head_dim], contiguous, on the GPU
+  q, o         bf16  [batch, heads, seq_len, head_dim], contiguous, on the GPU
+  k, v         bf16  [batch, kv_heads, seq_len, head_dim] (kv_heads divides heads)
   mass         fp32  [batch, heads, n_blocks, n_blocks]
   row_ptr      int32 [batch * heads * n_blocks + 1]
   col_idx      int32 [>= wise_select_max_nnz(...)]
