@@ -88,6 +88,18 @@ __device__ __forceinline__ void dma16(i32x4_t desc, uint32_t lds_base, uint32_t 
                : "memory", "m0");
 }
 
+// The same load without a compiler memory clobber, for loads into the stage
+// that no LDS access of the current step touches: LDS reads of the current
+// stage may then be scheduled across it.  It stays ordered with the
+// barriers (both are volatile side effects), and completion is waited for
+// explicitly as for dma16.
+__device__ __forceinline__ void dma16_free(i32x4_t desc, uint32_t lds_base, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(desc), "s"(soff)
+               : "m0");
+}
+
 template <int D, int BLK, int KT, int RPW = 1>
 struct AttnShape {
   static constexpr int kWaves = BLK / 32 * RPW;   // RPW rows of BLK queries per workgroup
@@ -492,7 +504,19 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   }
 
   // S^T = K Q^T for one key tile (Kt: the LDS slot holding its K rows).
-  auto scores = [&](f32x16_t (&sc)[Sh::kM], const uint16_t* Kt) __attribute__((always_inline)) {
+  // With nkey0 >= 0 (direct-to-LDS staging), this wave's loads of the next
+  // tile into stage nstage are spread over the QK^T MFMAs, one load per
+  // few MFMAs, instead of leaving every wave of the workgroup to issue all
+  // of them at once after the barrier.
+  auto scores_l = [&]<bool LOAD>(f32x16_t (&sc)[Sh::kM], const uint16_t* Kt, int nstage, int nkey0)
+                      __attribute__((always_inline)) {
+    constexpr int nQK = Sh::kM * Sh::kChunks;
+    constexpr int nLoad = 2 * Dm::kInstr;
+    uint32_t soff = 0, kbase = 0;
+    if (kDma && LOAD) {
+      soff = __builtin_amdgcn_readfirstlane((uint32_t)nkey0 * D * 2);
+      kbase = __builtin_amdgcn_readfirstlane(lds0 + nstage * Dm::kStageBytes + wave_u * 1024);
+    }
 #pragma unroll
     for (int m = 0; m < Sh::kM; ++m) {
 #pragma unroll
@@ -503,8 +527,20 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
                                   : Ks + (m * 32 + n) * Sh::kKsStride + c * 16 + 8 * g;
         const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kp);
         sc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], sc[m], 0, 0, 0);
+        if constexpr (kDma && LOAD) {
+          const int i = m * Sh::kChunks + c;
+#pragma unroll
+          for (int j = i * nLoad / nQK; j < (i + 1) * nLoad / nQK; ++j) {
+            if (j < Dm::kInstr) dma16_free(kdesc, kbase + j * Dm::kWaves * 1024, dk[j], soff);
+            else dma16_free(vdesc, kbase + (j - Dm::kInstr) * Dm::kWaves * 1024 + Dm::kTileBytes,
+                            dv[j - Dm::kInstr], soff);
+          }
+        }
       }
     }
+  };
+  auto scores = [&](f32x16_t (&sc)[Sh::kM], const uint16_t* Kt) __attribute__((always_inline)) {
+    scores_l.template operator()<false>(sc, Kt, 0, 0);
   };
 
   // Causal mask (diagonal block only), lazy-rescale check and rare rescale.
@@ -584,11 +620,12 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   // The MFMA stretches run at raised wave priority: when both waves of a
   // SIMD are ready, the one feeding the matrix core issues first and the
   // other's softmax work fills the MFMA shadow.
-  auto compute_tile = [&]<bool MASKED>(int kb, int sub, const uint16_t* Kt, const uint16_t* Vt,
-                                       uint32_t pairs) __attribute__((always_inline)) {
+  auto compute_tile = [&]<bool MASKED, bool LOAD = false>(int kb, int sub, const uint16_t* Kt, const uint16_t* Vt,
+                                                           uint32_t pairs, int nstage = 0, int nkey0 = 0)
+                          __attribute__((always_inline)) {
     f32x16_t sc[Sh::kM];
     __builtin_amdgcn_s_setprio(1);
-    scores(sc, Kt);
+    scores_l.template operator()<LOAD>(sc, Kt, nstage, nkey0);
     __builtin_amdgcn_s_setprio(0);
     if constexpr (LPR == 2 && MODE == kSparse) {
       // logical pairs this tile does not list: query half n/16, key half i/8
@@ -736,12 +773,19 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
       const int st = it & 1;
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       lds_barrier();
-      if (it + 1 < n_tiles) dma_tile(st ^ 1, tile_key0(it + 1));
       const uint16_t* Kt = reinterpret_cast<const uint16_t*>(smem + st * Dm::kStageBytes);
       const uint16_t* Vt = Kt + KT * D;
-      if (mine) {
+      // The next tile's loads ride along with this tile's QK^T MFMAs when
+      // this wave computes; a wave with nothing to compute issues them at once.
+      const int nkey0 = it + 1 < n_tiles ? tile_key0(it + 1) : -1;
+      if (mine && nkey0 >= 0) {
+        if (kb == qb) compute_tile.template operator()<true, true>(kb, sub, Kt, Vt, pairs, st ^ 1, nkey0);
+        else compute_tile.template operator()<false, true>(kb, sub, Kt, Vt, pairs, st ^ 1, nkey0);
+      } else if (mine) {
         if (kb == qb) compute_tile.template operator()<true>(kb, sub, Kt, Vt, pairs);
         else compute_tile.template operator()<false>(kb, sub, Kt, Vt, pairs);
+      } else if (nkey0 >= 0) {
+        dma_tile(st ^ 1, nkey0);
       }
     }
   } else {
