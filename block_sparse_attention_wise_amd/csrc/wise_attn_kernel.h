@@ -81,6 +81,11 @@ __device__ __forceinline__ i32x4_t buffer_desc(const void* base, uint32_t bytes)
 // LDS writes: completion is waited for explicitly (s_waitcnt vmcnt before
 // the barrier that publishes a stage), and LDS reads of the other stage
 // need not wait for them.
+// (The compiler warns that M0 is a reserved register; these two helpers are
+// the only code that writes it, and declaring the clobber is what keeps the
+// compiler from relying on an old M0 value afterwards.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(i32x4_t desc, uint32_t lds_base, uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
@@ -99,6 +104,7 @@ __device__ __forceinline__ void dma16_free(i32x4_t desc, uint32_t lds_base, uint
                : "s"(lds_base), "v"(voff), "s"(desc), "s"(soff)
                : "m0");
 }
+#pragma clang diagnostic pop
 
 template <int D, int BLK, int KT, int RPW = 1>
 struct AttnShape {
