@@ -514,10 +514,11 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   // tile into stage nstage are spread over the QK^T MFMAs, one load per
   // few MFMAs, instead of leaving every wave of the workgroup to issue all
   // of them at once after the barrier.
-  auto scores_l = [&]<bool LOAD>(f32x16_t (&sc)[Sh::kM], const uint16_t* Kt, int nstage, int nkey0)
+  // LOAD: 0 no loads, 1 the next tile's K and V, 2 its K only.
+  auto scores_l = [&]<int LOAD>(f32x16_t (&sc)[Sh::kM], const uint16_t* Kt, int nstage, int nkey0)
                       __attribute__((always_inline)) {
     constexpr int nQK = Sh::kM * Sh::kChunks;
-    constexpr int nLoad = 2 * Dm::kInstr;
+    constexpr int nLoad = (LOAD == 2 ? 1 : 2) * Dm::kInstr;
     uint32_t soff = 0, kbase = 0;
     if (kDma && LOAD) {
       soff = __builtin_amdgcn_readfirstlane((uint32_t)nkey0 * D * 2);
@@ -546,7 +547,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
     }
   };
   auto scores = [&](f32x16_t (&sc)[Sh::kM], const uint16_t* Kt) __attribute__((always_inline)) {
-    scores_l.template operator()<false>(sc, Kt, 0, 0);
+    scores_l.template operator()<0>(sc, Kt, 0, 0);
   };
 
   // Causal mask (diagonal block only), lazy-rescale check and rare rescale.
@@ -631,7 +632,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
                           __attribute__((always_inline)) {
     f32x16_t sc[Sh::kM];
     __builtin_amdgcn_s_setprio(1);
-    scores_l.template operator()<LOAD>(sc, Kt, nstage, nkey0);
+    scores_l.template operator()<LOAD ? 1 : 0>(sc, Kt, nstage, nkey0);
     __builtin_amdgcn_s_setprio(0);
     if constexpr (LPR == 2 && MODE == kSparse) {
       // logical pairs this tile does not list: query half n/16, key half i/8
@@ -646,9 +647,10 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   };
 
   // Two-pass mass mode, first pass: running max and fp32 row sum only.
-  auto sum_tile = [&]<bool MASKED>(int kb, int sub, const uint16_t* Kt) __attribute__((always_inline)) {
+  auto sum_tile = [&]<bool MASKED, bool LOAD = false>(int kb, int sub, const uint16_t* Kt, int nstage = 0,
+                                                       int nkey0 = 0) __attribute__((always_inline)) {
     f32x16_t sc[Sh::kM];
-    scores(sc, Kt);
+    scores_l.template operator()<LOAD ? 2 : 0>(sc, Kt, nstage, nkey0);
     prep.template operator()<MASKED>(kb, sub, sc);
     const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
     float tsum = 0.f;
@@ -662,10 +664,11 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   // Two-pass mass mode, second pass: P = exp2(s*scale*log2e - m) / l with
   // the final m and l of the first pass (fp32), summed into this wave's
   // slot of the key block, and rounded to bf16 for O^T += V^T P^T.
-  auto mass_tile = [&]<bool MASKED>(int kb, int sub, const uint16_t* Kt, const uint16_t* Vt,
-                                    float neg_m, float inv_l) __attribute__((always_inline)) {
+  auto mass_tile = [&]<bool MASKED, bool LOAD = false>(int kb, int sub, const uint16_t* Kt, const uint16_t* Vt,
+                                                        float neg_m, float inv_l, int nstage = 0, int nkey0 = 0)
+                       __attribute__((always_inline)) {
     f32x16_t sc[Sh::kM];
-    scores(sc, Kt);
+    scores_l.template operator()<LOAD ? 1 : 0>(sc, Kt, nstage, nkey0);
     if constexpr (MASKED) {
       const int rel = qrow - (kb * BLK + sub * KT);
 #pragma unroll
@@ -735,11 +738,16 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
       const int st = it & 1;
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       lds_barrier();
-      if (it + 1 < n_tiles) dma_k(st ^ 1, tile_key0(it + 1));
       const uint16_t* Kt = reinterpret_cast<const uint16_t*>(smem + st * Dm::kStageBytes);
-      if (mine) {
+      const int nkey0 = it + 1 < n_tiles ? tile_key0(it + 1) : -1;
+      if (mine && nkey0 >= 0) {
+        if (kb == qb) sum_tile.template operator()<true, true>(kb, sub, Kt, st ^ 1, nkey0);
+        else sum_tile.template operator()<false, true>(kb, sub, Kt, st ^ 1, nkey0);
+      } else if (mine) {
         if (kb == qb) sum_tile.template operator()<true>(kb, sub, Kt);
         else sum_tile.template operator()<false>(kb, sub, Kt);
+      } else if (nkey0 >= 0) {
+        dma_k(st ^ 1, nkey0);
       }
     }
     const float lt1 = l_part + __shfl_xor(l_part, 32);
@@ -757,12 +765,17 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
       const int st = it & 1;
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       lds_barrier();
-      if (it + 1 < n_tiles) dma_tile(st ^ 1, tile_key0(it + 1));
       const uint16_t* Kt = reinterpret_cast<const uint16_t*>(smem + st * Dm::kStageBytes);
       const uint16_t* Vt = Kt + KT * D;
-      if (mine) {
+      const int nkey0 = it + 1 < n_tiles ? tile_key0(it + 1) : -1;
+      if (mine && nkey0 >= 0) {
+        if (kb == qb) mass_tile.template operator()<true, true>(kb, sub, Kt, Vt, neg_m, inv_l, st ^ 1, nkey0);
+        else mass_tile.template operator()<false, true>(kb, sub, Kt, Vt, neg_m, inv_l, st ^ 1, nkey0);
+      } else if (mine) {
         if (kb == qb) mass_tile.template operator()<true>(kb, sub, Kt, Vt, neg_m, inv_l);
         else mass_tile.template operator()<false>(kb, sub, Kt, Vt, neg_m, inv_l);
+      } else if (nkey0 >= 0) {
+        dma_tile(st ^ 1, nkey0);
       }
     }
   } else if constexpr (kDma) {
