@@ -1,4 +1,8 @@
-// Flash-style causal attention kernel for gfx950 (CDNA4), bf16 MFMA.
+// Flash-style causal attention kernel for gfx950 (CDNA4), bf16 MFMA, for
+// the three attention steps of "Attention Routing Stabilizes Early:
+// Working-Set Inference for Recurrent Language Models" (WISE): dense causal
+// attention (Section 3, Eq. 2), the same with the block mass of Section 5.1,
+// Eq. (5), and attention inside the working set (Section 5.2, Eq. 7-8).
 //
 // A workgroup owns RPW adjacent rows = (batch*head, query block q) of
 // B = BLK queries each; the waves of a row own 32 queries apiece.  The

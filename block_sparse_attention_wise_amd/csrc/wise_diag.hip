@@ -1,5 +1,6 @@
-// Working-set diagnostics (WISE, Section 7 "Evaluation metrics"; Appendix
-// C.2, Eq. 23-25).
+// Working-set diagnostics ("Attention Routing Stabilizes Early: Working-Set
+// Inference for Recurrent Language Models" (WISE), Section 7 "Evaluation
+// metrics"; Appendix C.2, Eq. 23-25).
 //
 //  * Retained future attention mass: for a row r = (b, h, q) and an
 //    unrestricted step's block masses r_qb (Eq. 5, rows summing to 1), the

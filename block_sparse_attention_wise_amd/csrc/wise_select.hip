@@ -1,4 +1,6 @@
-// Working-set selection (WISE, Section 5.1, Eq. 6; Appendix A.1, Eq. 12).
+// Working-set selection ("Attention Routing Stabilizes Early: Working-Set
+// Inference for Recurrent Language Models" (WISE), Section 5.1, Eq. 6;
+// Appendix A.1, Eq. 12).
 //
 // One wavefront per row (batch, head, query block q) chooses, among the
 // admissible key blocks 0..q, the smallest set whose mean discovery mass
