@@ -168,8 +168,9 @@ __host__ __device__ constexpr bool uses_dma() { return MODE != kDenseMass; }
 
 // Rows (query blocks) per workgroup: two adjacent rows for block 64, so
 // that four waves share every staged K/V tile (the two rows' key-block
-// lists overlap heavily), one row otherwise.  The mass mode keeps one row
-// when the per-(query, key block) partials of two rows would not fit.
+// lists overlap heavily), several one-wave rows for block 32 (rpw32), one
+// row for block 128.  The mass mode keeps one row when the per-(query, key
+// block) partials of two rows would not fit.
 // nblk: physical blocks of BLK keys; LPR logical blocks of BLK/LPR keys per
 // physical block (LPR = 2 runs block 16 on 32 x 32 tiles).
 template <int D, int BLK, int KT, int RPW, int LPR = 1>
@@ -514,11 +515,11 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   }
 
   // S^T = K Q^T for one key tile (Kt: the LDS slot holding its K rows).
-  // With nkey0 >= 0 (direct-to-LDS staging), this wave's loads of the next
-  // tile into stage nstage are spread over the QK^T MFMAs, one load per
-  // few MFMAs, instead of leaving every wave of the workgroup to issue all
-  // of them at once after the barrier.
-  // LOAD: 0 no loads, 1 the next tile's K and V, 2 its K only.
+  // With LOAD (direct-to-LDS staging), this wave's loads of the next tile
+  // (keys from nkey0, into stage nstage) are spread over the QK^T MFMAs, one
+  // load per few MFMAs, instead of leaving every wave of the workgroup to
+  // issue all of them at once after the barrier.  LOAD: 0 no loads, 1 the
+  // next tile's K and V, 2 its K only.
   auto scores_l = [&]<int LOAD>(f32x16_t (&sc)[Sh::kM], const uint16_t* Kt, int nstage, int nkey0)
                       __attribute__((always_inline)) {
     constexpr int nQK = Sh::kM * Sh::kChunks;
