@@ -87,11 +87,17 @@ KERNEL_SOURCES = ["block_sparse_attention_wise_amd/csrc/wise_attn_kernel.h",
 
 
 def kernel_source_hash() -> str:
+    """Hash of the attention kernel's code: line comments and blank lines are
+    left out, so that editing a comment does not retire the counter record."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            for line in fh:
+                code = re.sub(r"//.*$", "", line).rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
