@@ -215,10 +215,14 @@ __device__ __forceinline__ void store_rows(uint16_t* dst, int tid,
 
 // Scores of one key tile: causal mask (MASKED: diagonal block only), the
 // lazy-rescale check, and the rare rescale of everything accumulated so far.
+// Returns the larger of run_max and this lane's largest (masked) raw score
+// of the tile.  Passing the lane's running raw maximum as run_max cannot
+// trigger a rescale by itself: that maximum, scaled, never exceeds the
+// reference by more than the threshold.
 template <int D, int BLK, int KT, int MODE, bool MASKED>
-__device__ __forceinline__ void softmax_prep(float* part, float scale_log2, int rel, int g, int n,
+__device__ __forceinline__ float softmax_prep(float* part, float scale_log2, int rel, int g, int n,
                                              int wave, int kb, float& m_ref, float& l_part,
-                                             float& blk_part,
+                                             float& blk_part, float run_max,
                                              f32x16_t (&s)[AttnShape<D, BLK, KT>::kM],
                                              f32x16_t (&oacc)[AttnShape<D, BLK, KT>::kDTiles]) {
   using Sh = AttnShape<D, BLK, KT>;
@@ -232,7 +236,7 @@ __device__ __forceinline__ void softmax_prep(float* part, float scale_log2, int 
         s[m][i] = (koff > rel) ? -INFINITY : s[m][i];
       }
   }
-  float tmax = -INFINITY;
+  float tmax = run_max;
 #pragma unroll
   for (int m = 0; m < Sh::kM; ++m)
 #pragma unroll
@@ -257,6 +261,7 @@ __device__ __forceinline__ void softmax_prep(float* part, float scale_log2, int 
     }
     m_ref = m_new;
   }
+  return tmax;
 }
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -480,6 +485,8 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
     for (int i = 0; i < 16; ++i) oacc[t][i] = 0.f;
   float m_ref = -INFINITY;  // identical in both lanes of a query
   float l_part = 0.f;       // this lane's share of the row sum
+  float m_hi = -INFINITY;   // mass modes: this lane's largest raw score so far
+  float l_two = 0.f;        // two-pass: row sum relative to the exact max
   float blk_part = 0.f;     // this lane's share of the current key block's mass
 
   u32x4_t kreg[Sh::kPer];
@@ -557,8 +564,10 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
 
   // Causal mask (diagonal block only), lazy-rescale check and rare rescale.
   auto prep = [&]<bool MASKED>(int kb, int sub, f32x16_t (&sc)[Sh::kM]) __attribute__((always_inline)) {
-    softmax_prep<D, BLK, KT, MODE, MASKED>(part, p.scale_log2, qrow - (kb * BLK + sub * KT), g, n, wr,
-                                           kb * LPR, m_ref, l_part, blk_part, sc, oacc);
+    constexpr bool kTrack = (MODE == kDenseMass || MODE == kMassTwoPass);
+    return softmax_prep<D, BLK, KT, MODE, MASKED>(part, p.scale_log2, qrow - (kb * BLK + sub * KT), g, n, wr,
+                                                  kb * LPR, m_ref, l_part, blk_part,
+                                                  kTrack ? m_hi : -INFINITY, sc, oacc);
   };
 
   // P = exp2(s * scale*log2e - m) per 32-key sub-tile, then that
@@ -583,7 +592,11 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
         }
       if constexpr (MODE != kDenseMass) {
         // Row sum of the bf16 operands themselves (the same values the PV
-        // product uses), two per packed dot product.
+        // product uses), two per packed dot product.  O is divided by this
+        // sum: the weights then add up to one however P was rounded, so the
+        // rounding error of a dominant weight is damped by one minus that
+        // weight.  (The mass mode needs the fp32 sum for the block mass; its
+        // divisor is fixed up in the epilogue instead.)
         const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
@@ -647,16 +660,18 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
           if (!((pairs >> (2 * (n >> 4) + (i >> 3))) & 1u)) sc[0][i] = -INFINITY;
       }
     }
-    prep.template operator()<MASKED>(kb, sub, sc);
+    const float run_max = prep.template operator()<MASKED>(kb, sub, sc);
+    if constexpr (MODE == kDenseMass) m_hi = run_max;
     expv(kb, sub, sc, Vt);
   };
 
-  // Two-pass mass mode, first pass: running max and fp32 row sum only.
+  // Two-pass mass mode, first pass: running max, fp32 row sum and the
+  // exact largest score.
   auto sum_tile = [&]<bool MASKED, bool LOAD = false>(int kb, int sub, const uint16_t* Kt, int nstage = 0,
                                                        int nkey0 = 0) __attribute__((always_inline)) {
     f32x16_t sc[Sh::kM];
     scores_l.template operator()<LOAD ? 2 : 0>(sc, Kt, nstage, nkey0);
-    prep.template operator()<MASKED>(kb, sub, sc);
+    m_hi = prep.template operator()<MASKED>(kb, sub, sc);
     const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
     float tsum = 0.f;
 #pragma unroll
@@ -666,9 +681,13 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
     l_part += tsum;
   };
 
-  // Two-pass mass mode, second pass: P = exp2(s*scale*log2e - m) / l with
-  // the final m and l of the first pass (fp32), summed into this wave's
-  // slot of the key block, and rounded to bf16 for O^T += V^T P^T.
+  // Two-pass mass mode, second pass: p = exp2(s*scale*log2e - m) with m the
+  // row's exact largest scaled score, so the largest p is exactly 1 in bf16.
+  // The block mass is the fp32 sum of p times 1/l (l: the first pass's fp32
+  // row sum, brought to m), added to this wave's slot of the key block.
+  // O^T += V^T P^T takes p rounded to bf16; O is divided by l at the end.
+  // (Feeding p/l instead saves that division but rounds the dominant
+  // weight itself, whose error then reaches O undamped.)
   auto mass_tile = [&]<bool MASKED, bool LOAD = false>(int kb, int sub, const uint16_t* Kt, const uint16_t* Vt,
                                                         float neg_m, float inv_l, int nstage = 0, int nkey0 = 0)
                        __attribute__((always_inline)) {
@@ -693,7 +712,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sc[m][kk * 8 + e], p.scale_log2, neg_m)) * inv_l;
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sc[m][kk * 8 + e], p.scale_log2, neg_m));
           tsum += pv;
           if constexpr (LPR == 2) hs[kk] += pv;
           pf[kk][e] = (__bf16)pv;
@@ -714,6 +733,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
     }
     if constexpr (LPR == 1) {
       // sum over the wave's 32 queries x 2 lane halves, fixed butterfly order
+      tsum *= inv_l;
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) tsum += __shfl_xor(tsum, off);
       if (lane == 0) slots[(slot * lnb + kb) * WR + wr] += tsum;
@@ -721,7 +741,8 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
       // per (logical query block = query half, logical key block = key half)
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
-        float v = hs[kh] + __shfl_xor(hs[kh], 32);
+        float v = hs[kh] * inv_l;
+        v += __shfl_xor(v, 32);
 #pragma unroll
         for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off);
         if ((lane & 47) == 0)   // lanes 0 and 16
@@ -755,9 +776,13 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
         dma_k(st ^ 1, nkey0);
       }
     }
-    const float lt1 = l_part + __shfl_xor(l_part, 32);
-    const float inv_l = lt1 > 0.f ? 1.f / lt1 : 0.f;
-    const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
+    // Bring the row sum from the lazy reference to the exact max.
+    const float mh = fmaxf(m_hi, __shfl_xor(m_hi, 32));
+    const float m_ex = mh * p.scale_log2;
+    l_two = (mh == -INFINITY) ? 0.f
+                              : (l_part + __shfl_xor(l_part, 32)) * __builtin_amdgcn_exp2f(m_ref - m_ex);
+    const float inv_l = l_two > 0.f ? 1.f / l_two : 0.f;
+    const float neg_m = (mh == -INFINITY) ? 0.f : -m_ex;
     // Second pass over the same tiles with K and V.
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     lds_barrier();
@@ -839,18 +864,36 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   }
 
   // ---- epilogue -----------------------------------------------------------
-  const float lt = l_part + __shfl_xor(l_part, 32);
-  const float inv = (MODE == kMassTwoPass) ? 1.f : (lt > 0.f ? 1.f / lt : 0.f);   // two-pass O is normalised
+  const float lt = (MODE == kMassTwoPass) ? l_two : l_part + __shfl_xor(l_part, 32);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  // O's divisor.  The one-pass mass mode sums fp32 p for the block mass; O
+  // is divided by that sum with the row's largest term counted at its bf16
+  // value, the one the PV product used, so that the dominant weight's
+  // rounding error is damped as in the other modes.  That term was taken
+  // against the final reference max: a later tile can raise the reference
+  // only with a score above this one.  (Lanes of a query that hold an equal
+  // largest score each count theirs.)
+  float lo = lt;
+  if constexpr (MODE == kDenseMass) {
+    const float mh = fmaxf(m_hi, __shfl_xor(m_hi, 32));
+    float d = 0.f;
+    if (mh != -INFINITY && m_hi == mh) {
+      const float pm = __builtin_amdgcn_exp2f(fmaf(m_hi, p.scale_log2, -m_ref));
+      d = (float)(__bf16)pm - pm;
+    }
+    lo = lt + (d + __shfl_xor(d, 32));
+  }
+  const float inv_o = lo > 0.f ? 1.f / lo : 0.f;
   if (row_ok) {
     uint16_t* Oh = p.o + head_off + (size_t)qrow * D;
 #pragma unroll
     for (int t = 0; t < Sh::kDTiles; ++t)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        __bf16 b0 = (__bf16)(oacc[t][4 * j + 0] * inv);
-        __bf16 b1 = (__bf16)(oacc[t][4 * j + 1] * inv);
-        __bf16 b2 = (__bf16)(oacc[t][4 * j + 2] * inv);
-        __bf16 b3 = (__bf16)(oacc[t][4 * j + 3] * inv);
+        __bf16 b0 = (__bf16)(oacc[t][4 * j + 0] * inv_o);
+        __bf16 b1 = (__bf16)(oacc[t][4 * j + 1] * inv_o);
+        __bf16 b2 = (__bf16)(oacc[t][4 * j + 2] * inv_o);
+        __bf16 b3 = (__bf16)(oacc[t][4 * j + 3] * inv_o);
         u32x2_t w;
         w.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
         w.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
@@ -1038,7 +1081,7 @@ int fused_mass_waves(int nblk) {
 // The mass launch runs in one pass (O and the block mass from the same P,
 // with nB x (B+1) fp32 partials per row in LDS) unless those partials leave
 // fewer than WISE_TWO_PASS_BELOW_WAVES resident waves per CU; then it runs
-// in two passes over the keys (row max and sum, then normalised P), which
+// in two passes over the keys (row max and sum, then P, O and the mass), which
 // needs only one fp32 per (row, key block, wave) of LDS.
 // The one-pass mass kernel with one 32-query wave per workgroup stages a
 // whole 32-key tile per lane in VGPRs; at head_dim 128 that spills.

@@ -13,7 +13,7 @@ enum AttnMode : int {
   kDenseMass = 1,   // Eq. (2) plus the block mass of Eq. (5), added into `mass`
   kSparse = 2,      // Eq. (8): only the key blocks listed in the CSR row
   kMassTwoPass = 3  // kDenseMass in two passes over the keys (launcher's choice
-                    // for long rows): row max and sum first, then normalised P
+                    // for long rows): row max and sum first, then P, O and mass
 };
 
 struct AttnParams {
