@@ -1,8 +1,9 @@
 """Python binding of libwise, the WISE working-set attention library (gfx950).
 
 Thin argument marshalling over the C ABI in ``include/wise.h``: every
-function here checks tensor dtypes/shapes/devices, passes raw device
-pointers and the current HIP stream, and turns a non-zero status into
+function here checks tensor dtypes/shapes/devices (all on one GPU), makes
+that GPU current for the call, passes raw device pointers and the stream
+(default: that GPU's current HIP stream), and turns a non-zero status into
 ``WiseError``.  All computation runs in the HIP kernels of ``libwise.so``;
 there is no fallback path.  Build the library with
 ``python -m block_sparse_attention_wise_amd.build``.
@@ -101,6 +102,18 @@ def _check(status: int, func: str) -> None:
         raise WiseError(status, func, detail)
 
 
+def _call(func: str, device, stream, *args) -> None:
+    """Run one library call with ``device`` current (the library launches on
+    the current device) on ``stream`` (default: that device's current
+    stream), and raise on a non-zero status."""
+    torch = _torch()
+    lib = load_library()
+    with torch.cuda.device(device):
+        st = getattr(lib, func)(*args, _stream_ptr(stream))
+        if st != WISE_OK:
+            _check(st, func)
+
+
 def _torch():
     import torch
     return torch
@@ -124,6 +137,22 @@ def _need(t, name, dtype, ndim=None):
         raise ValueError(f"{name} must be contiguous")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def _same_device(*named):
+    """Every tensor on the first one's device; returns that device."""
+    dev = named[0][0].device
+    for t, n in named[1:]:
+        if t.device != dev:
+            raise ValueError(f"{n} is on {t.device}, {named[0][1]} on {dev}: all tensors must share one GPU")
+    return dev
+
+
+def _block(block_size) -> int:
+    b = int(block_size)
+    if b <= 0:
+        raise ValueError(f"block_size must be positive, got {block_size}")
+    return b
 
 
 def _desc(q, block_size: int, softmax_scale: float, k=None) -> WiseDesc:
@@ -158,18 +187,21 @@ def wise_full_attn(q, k, v, block_size: int, o=None, lse=None, softmax_scale: fl
                    stream=None):
     """Dense causal attention (Eq. 2).  Returns o (bf16)."""
     torch = _torch()
+    block_size = _block(block_size)
     _qkv(q, k, v)
     o = _out(o, q)
     lse_ptr = None
+    named = [(q, "q"), (k, "k"), (v, "v"), (o, "o")]
     if lse is not None:
         _need(lse, "lse", torch.float32, 3)
         if tuple(lse.shape) != tuple(q.shape[:3]):
             raise ValueError("lse must be [batch, heads, seq_len]")
         lse_ptr = lse.data_ptr()
+        named.append((lse, "lse"))
+    dev = _same_device(*named)
     d = _desc(q, block_size, softmax_scale, k)
-    st = load_library().wise_full_attn(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                       o.data_ptr(), lse_ptr, _stream_ptr(stream))
-    _check(st, "wise_full_attn")
+    _call("wise_full_attn", dev, stream, ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+          o.data_ptr(), lse_ptr)
     return o
 
 
@@ -183,16 +215,16 @@ def wise_full_attn_accum(q, k, v, mass, block_size: int, o=None, softmax_scale: 
                          stream=None):
     """Discovery step: dense attention + block mass (Eq. 2, 5) added into ``mass``."""
     torch = _torch()
+    block_size = _block(block_size)
     _qkv(q, k, v)
     _need(mass, "mass", torch.float32, 4)
     if tuple(mass.shape) != _mass_shape(q, block_size):
         raise ValueError(f"mass must be {_mass_shape(q, block_size)}, got {tuple(mass.shape)}")
     o = _out(o, q)
+    dev = _same_device((q, "q"), (k, "k"), (v, "v"), (o, "o"), (mass, "mass"))
     d = _desc(q, block_size, softmax_scale, k)
-    st = load_library().wise_full_attn_accum(ctypes.byref(d), q.data_ptr(), k.data_ptr(),
-                                             v.data_ptr(), o.data_ptr(), mass.data_ptr(),
-                                             _stream_ptr(stream))
-    _check(st, "wise_full_attn_accum")
+    _call("wise_full_attn_accum", dev, stream, ctypes.byref(d), q.data_ptr(), k.data_ptr(),
+          v.data_ptr(), o.data_ptr(), mass.data_ptr())
     return o
 
 
@@ -214,6 +246,7 @@ def wise_select_support(mass, n_steps: int, eta: float, head_dim: int, block_siz
     are meaningful.
     """
     torch = _torch()
+    block_size = _block(block_size)
     _need(mass, "mass", torch.float32, 4)
     b, h, nb, nb2 = mass.shape
     if nb != nb2:
@@ -230,11 +263,9 @@ def wise_select_support(mass, n_steps: int, eta: float, head_dim: int, block_siz
     _need(col_idx, "col_idx", torch.int32, 1)
     if row_ptr.numel() != n_rows + 1:
         raise ValueError(f"row_ptr must have {n_rows + 1} entries")
-    st = load_library().wise_select_support(ctypes.byref(d), mass.data_ptr(), int(n_steps),
-                                            float(eta), int(max_blocks), row_ptr.data_ptr(),
-                                            col_idx.data_ptr(), col_idx.numel(),
-                                            _stream_ptr(stream))
-    _check(st, "wise_select_support")
+    dev = _same_device((mass, "mass"), (row_ptr, "row_ptr"), (col_idx, "col_idx"))
+    _call("wise_select_support", dev, stream, ctypes.byref(d), mass.data_ptr(), int(n_steps),
+          float(eta), int(max_blocks), row_ptr.data_ptr(), col_idx.data_ptr(), col_idx.numel())
     return row_ptr, col_idx
 
 
@@ -247,6 +278,7 @@ def wise_select_variant(kind: int, step_mass, eta: float, head_dim: int, block_s
     over single-step masses ``step_mass`` [n_mass, batch, heads, nB, nB]
     -> (row_ptr, col_idx) CSR."""
     torch = _torch()
+    block_size = _block(block_size)
     _need(step_mass, "step_mass", torch.float32, 5)
     n_mass, b, h, nb, nb2 = step_mass.shape
     if nb != nb2:
@@ -263,10 +295,9 @@ def wise_select_variant(kind: int, step_mass, eta: float, head_dim: int, block_s
     _need(col_idx, "col_idx", torch.int32, 1)
     if row_ptr.numel() != n_rows + 1:
         raise ValueError(f"row_ptr must have {n_rows + 1} entries")
-    st = load_library().wise_select_variant(ctypes.byref(d), int(kind), step_mass.data_ptr(), int(n_mass),
-                                            float(eta), row_ptr.data_ptr(), col_idx.data_ptr(),
-                                            col_idx.numel(), _stream_ptr(stream))
-    _check(st, "wise_select_variant")
+    dev = _same_device((step_mass, "step_mass"), (row_ptr, "row_ptr"), (col_idx, "col_idx"))
+    _call("wise_select_variant", dev, stream, ctypes.byref(d), int(kind), step_mass.data_ptr(), int(n_mass),
+          float(eta), row_ptr.data_ptr(), col_idx.data_ptr(), col_idx.numel())
     return row_ptr, col_idx
 
 
@@ -274,6 +305,7 @@ def wise_support_mass(mass, row_ptr, col_idx, head_dim: int, block_size: int, re
     """Per-row mass of ``mass`` [batch, heads, nB, nB] inside the CSR support
     -> fp32 [batch * heads * nB] (retained future attention mass)."""
     torch = _torch()
+    block_size = _block(block_size)
     _need(mass, "mass", torch.float32, 4)
     _need(row_ptr, "row_ptr", torch.int32, 1)
     _need(col_idx, "col_idx", torch.int32, 1)
@@ -284,10 +316,12 @@ def wise_support_mass(mass, row_ptr, col_idx, head_dim: int, block_size: int, re
     if retained is None:
         retained = torch.empty(n_rows, dtype=torch.float32, device=mass.device)
     _need(retained, "retained", torch.float32, 1)
+    if retained.numel() != n_rows:
+        raise ValueError(f"retained must have {n_rows} entries")
+    dev = _same_device((mass, "mass"), (row_ptr, "row_ptr"), (col_idx, "col_idx"), (retained, "retained"))
     d = WiseDesc(b, h, nb * block_size, head_dim, block_size, 0.0)
-    st = load_library().wise_support_mass(ctypes.byref(d), mass.data_ptr(), row_ptr.data_ptr(),
-                                          col_idx.data_ptr(), retained.data_ptr(), _stream_ptr(stream))
-    _check(st, "wise_support_mass")
+    _call("wise_support_mass", dev, stream, ctypes.byref(d), mass.data_ptr(), row_ptr.data_ptr(),
+          col_idx.data_ptr(), retained.data_ptr())
     return retained
 
 
@@ -295,19 +329,19 @@ def wise_support_overlap(csr_a, csr_b, batch: int, heads: int, n_blocks: int, he
                          block_size: int, stream=None):
     """Per-row |A & B| and |A | B| of two CSR supports -> (n_inter, n_union) int32."""
     torch = _torch()
+    block_size = _block(block_size)
     (ra, ca), (rb, cb) = csr_a, csr_b
     for t, n in ((ra, "row_ptr_a"), (ca, "col_idx_a"), (rb, "row_ptr_b"), (cb, "col_idx_b")):
         _need(t, n, torch.int32, 1)
     n_rows = batch * heads * n_blocks
     if ra.numel() != n_rows + 1 or rb.numel() != n_rows + 1:
         raise ValueError(f"row_ptr arrays must have {n_rows + 1} entries")
-    inter = torch.empty(n_rows, dtype=torch.int32, device=ra.device)
-    uni = torch.empty(n_rows, dtype=torch.int32, device=ra.device)
+    dev = _same_device((ra, "row_ptr_a"), (ca, "col_idx_a"), (rb, "row_ptr_b"), (cb, "col_idx_b"))
+    inter = torch.empty(n_rows, dtype=torch.int32, device=dev)
+    uni = torch.empty(n_rows, dtype=torch.int32, device=dev)
     d = WiseDesc(batch, heads, n_blocks * block_size, head_dim, block_size, 0.0)
-    st = load_library().wise_support_overlap(ctypes.byref(d), ra.data_ptr(), ca.data_ptr(), rb.data_ptr(),
-                                             cb.data_ptr(), inter.data_ptr(), uni.data_ptr(),
-                                             _stream_ptr(stream))
-    _check(st, "wise_support_overlap")
+    _call("wise_support_overlap", dev, stream, ctypes.byref(d), ra.data_ptr(), ca.data_ptr(), rb.data_ptr(),
+          cb.data_ptr(), inter.data_ptr(), uni.data_ptr())
     return inter, uni
 
 
@@ -315,6 +349,7 @@ def wise_sparse_attn(q, k, v, row_ptr, col_idx, block_size: int, o=None,
                      softmax_scale: float = 0.0, stream=None):
     """Reuse step: attention restricted to the CSR block support (Eq. 7-8)."""
     torch = _torch()
+    block_size = _block(block_size)
     _qkv(q, k, v)
     _need(row_ptr, "row_ptr", torch.int32, 1)
     _need(col_idx, "col_idx", torch.int32, 1)
@@ -322,11 +357,10 @@ def wise_sparse_attn(q, k, v, row_ptr, col_idx, block_size: int, o=None,
     if row_ptr.numel() != b * h * (s // block_size) + 1:
         raise ValueError("row_ptr must have batch*heads*n_blocks + 1 entries")
     o = _out(o, q)
+    dev = _same_device((q, "q"), (k, "k"), (v, "v"), (o, "o"), (row_ptr, "row_ptr"), (col_idx, "col_idx"))
     d = _desc(q, block_size, softmax_scale, k)
-    st = load_library().wise_sparse_attn(ctypes.byref(d), q.data_ptr(), k.data_ptr(),
-                                         v.data_ptr(), row_ptr.data_ptr(), col_idx.data_ptr(),
-                                         o.data_ptr(), _stream_ptr(stream))
-    _check(st, "wise_sparse_attn")
+    _call("wise_sparse_attn", dev, stream, ctypes.byref(d), q.data_ptr(), k.data_ptr(),
+          v.data_ptr(), row_ptr.data_ptr(), col_idx.data_ptr(), o.data_ptr())
     return o
 
 

@@ -424,7 +424,8 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
         const int lrow = row * LPR + lr, lq = qb * LPR + lr;   // logical row and query block
         int e_begin = p.row_ptr[lrow];
         int e_end = p.row_ptr[lrow + 1];
-        if (e_end < e_begin) e_end = e_begin;
+        if (e_begin < 0) e_begin = 0;         // malformed pointers: read nothing before col_idx
+        if (e_end < e_begin) e_end = e_begin; // and a decreasing pair as an empty row
         uint32_t* rb = bits + (slot * LPR + lr) * nwords;
         for (int idx = e_begin + lane; idx < e_end; idx += 64) {
           const int c = p.col_idx[idx];

@@ -177,8 +177,12 @@ wise_status_t wise_select_variant(const wise_attn_desc_t* desc, int32_t kind, co
  *          row's entries are read as a set of key blocks: entries outside
  *          [0, q] are ignored, repeated entries count once and their order
  *          does not matter.  A query with no admissible key in its row's
- *          blocks gets a zero output.  col_idx must hold row_ptr[n_rows]
- *          readable entries.
+ *          blocks gets a zero output.  The caller keeps every row_ptr
+ *          value within [0, length of col_idx]; row r reads col_idx
+ *          [row_ptr[r], row_ptr[r+1]).  A negative start is read as 0 and
+ *          a row whose end lies below its start as empty, so malformed
+ *          pointers cannot make the kernel read before col_idx; a value
+ *          past its end can, and is the caller's error.
  */
 wise_status_t wise_sparse_attn(const wise_attn_desc_t* desc, const void* q, const void* k,
                                const void* v, const int32_t* row_ptr, const int32_t* col_idx,
