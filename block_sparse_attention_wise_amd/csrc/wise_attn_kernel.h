@@ -21,11 +21,15 @@
 // S^T (lane = query, 16 keys per lane) coincide with the B-operand layout
 // the PV product needs, so P never leaves registers.
 //
-// Softmax: the reference max m of a query is only raised when a new score
-// exceeds it by more than 2^kTau (in log2 units); otherwise P may grow up to
-// 2^kTau, which fp32 accumulators and bf16 P operands absorb without loss
-// of relative precision.  This keeps the per-tile cross-lane max reduction
-// off the common path.  The block mass of Eq. (5) reuses the same fp32 P:
+// Softmax: the reference max m of a query is only raised when a new scaled
+// score exceeds it by more than kTau (log2 units); otherwise P may grow up
+// to 2^kTau.  bf16 P operands share fp32's exponent range and the O, l and
+// mass accumulators are fp32, so even 2^64 loses no relative precision and
+// leaves O far from overflow (2^64 x 2^16 keys x |v|).  A wide slack keeps
+// the rescale of O (a multiply per accumulator) and the cross-lane max
+// reduction off the common path: with attention logits that keep growing
+// along the key walk, a slack of 8 rescaled on 43% of 64-key wave tiles,
+// 64 only on each wave's first tile.  The block mass of Eq. (5) reuses the same fp32 P:
 // each (query, key block) partial sum is stored in LDS relative to m and
 // normalised by the query's final row sum in the epilogue.
 #pragma once
@@ -43,7 +47,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr float kTau = 8.0f;  // lazy-rescale slack, log2 units
+constexpr float kTau = 64.0f;  // lazy-rescale slack, log2 units
 
 // (a.lo16, b.lo16) and (a.hi16, b.hi16) as packed 32-bit words (one v_perm_b32).
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
@@ -248,16 +252,20 @@ __device__ __forceinline__ float softmax_prep(float* part, float scale_log2, int
     // rescale everything accumulated relative to the old one.
     const float rmax = fmaxf(tmax2, __shfl_xor(tmax2, 32));
     const float m_new = (rmax > m_ref + kTau) ? rmax : m_ref;
-    const float f = (m_new == m_ref) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+    // While a query's reference is still -inf nothing has been accumulated
+    // for it, so a wave whose queries all start here has nothing to rescale.
+    if (!__all(m_ref == -INFINITY)) {
+      const float f = (m_new == m_ref) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
 #pragma unroll
-    for (int t = 0; t < Sh::kDTiles; ++t)
+      for (int t = 0; t < Sh::kDTiles; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[t][i] *= f;
-    l_part *= f;
-    if constexpr (MODE == kDenseMass) {
-      blk_part *= f;
-      if (g == 0 && f != 1.f)
-        for (int b = 0; b < kb; ++b) part[b * (BLK + 1) + wave * 32 + n] *= f;
+        for (int i = 0; i < 16; ++i) oacc[t][i] *= f;
+      l_part *= f;
+      if constexpr (MODE == kDenseMass) {
+        blk_part *= f;
+        if (g == 0 && f != 1.f)
+          for (int b = 0; b < kb; ++b) part[b * (BLK + 1) + wave * 32 + n] *= f;
+      }
     }
     m_ref = m_new;
   }
