@@ -202,13 +202,17 @@ def main(argv=None):
     col_idx = torch.empty(cap, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    # Discovery steps keep their block-mass partials in a device workspace
+    # (allocated once, outside the timed region).
+    ws = torch.empty(max(wise.wise_accum_workspace_bytes(cfg.batch, cfg.heads, cfg.seq_len, D, B), 16),
+                     dtype=torch.uint8, device=dev)
 
     def trajectory(record=False):
         if record:
             ev[0].record(stream)
         mass.zero_()
         for t in range(td):
-            wise.wise_full_attn_accum(qs[t], ks[t], vs[t], mass, B, o=outs[t])
+            wise.wise_full_attn_accum_ws(qs[t], ks[t], vs[t], mass, B, o=outs[t], workspace=ws)
         if record:
             ev[1].record(stream)
         wise.wise_select_support(mass, td, cfg.eta, D, B, cfg.cap, row_ptr=row_ptr, col_idx=col_idx)
@@ -308,7 +312,7 @@ def main(argv=None):
     if not args.no_variants:
         step_mass = torch.zeros(td, cfg.batch, cfg.heads, nb, nb, dtype=torch.float32, device=dev)
         for t in range(td):
-            wise.wise_full_attn_accum(qs[t], ks[t], vs[t], step_mass[t], B, o=outs[t])
+            wise.wise_full_attn_accum_ws(qs[t], ks[t], vs[t], step_mass[t], B, o=outs[t], workspace=ws)
         win = step_mass[td - min(4, td):td].contiguous()
         first = step_mass[:1].contiguous()
         ctrl = torch.cat([first, win]).contiguous()
@@ -340,7 +344,7 @@ def main(argv=None):
         # switch (Eq. 24) and the switch-vs-final Jaccard (Eq. 25).
         late_mass = torch.zeros(T - td, cfg.batch, cfg.heads, nb, nb, dtype=torch.float32, device=dev)
         for t in range(td, T):
-            wise.wise_full_attn_accum(qs[t], ks[t], vs[t], late_mass[t - td], B, o=outs[t])
+            wise.wise_full_attn_accum_ws(qs[t], ks[t], vs[t], late_mass[t - td], B, o=outs[t], workspace=ws)
         sel_union = wise.wise_select_variant(wise.SELECT_UNION, win, cfg.eta, D, B)
 
         def retained(csr):

@@ -22,7 +22,8 @@ import os
 from typing import Optional, Tuple
 
 __all__ = ["WiseError", "WiseDesc", "load_library", "library_path", "wise_full_attn",
-           "wise_full_attn_accum", "wise_select_support", "wise_select_variant", "wise_sparse_attn",
+           "wise_full_attn_accum", "wise_full_attn_accum_ws", "wise_accum_workspace_bytes",
+           "wise_select_support", "wise_select_variant", "wise_sparse_attn",
            "SELECT_UNION", "SELECT_STATIC", "SELECT_MASS_MATCHED", "SELECT_SIZE_MATCHED",
            "wise_support_mass", "wise_support_overlap",
            "wise_select_max_nnz", "wise_abi_version", "WISE_OK", "WISE_ERR_INVALID_ARG",
@@ -72,6 +73,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     sigs = {
         "wise_full_attn": ([dp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "wise_full_attn_accum": ([dp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+        "wise_full_attn_accum_ws": ([dp, vp, vp, vp, vp, vp, vp, i64, vp], ctypes.c_int),
+        "wise_full_attn_accum_workspace_bytes": ([dp], i64),
         "wise_select_support": ([dp, vp, i32, ctypes.c_double, i32, vp, vp, i64, vp], ctypes.c_int),
         "wise_select_variant": ([dp, i32, vp, i32, ctypes.c_double, vp, vp, i64, vp], ctypes.c_int),
         "wise_support_mass": ([dp, vp, vp, vp, vp, vp], ctypes.c_int),
@@ -225,6 +228,45 @@ def wise_full_attn_accum(q, k, v, mass, block_size: int, o=None, softmax_scale: 
     d = _desc(q, block_size, softmax_scale, k)
     _call("wise_full_attn_accum", dev, stream, ctypes.byref(d), q.data_ptr(), k.data_ptr(),
           v.data_ptr(), o.data_ptr(), mass.data_ptr())
+    return o
+
+
+def wise_accum_workspace_bytes(batch: int, heads: int, seq_len: int, head_dim: int, block_size: int) -> int:
+    """Bytes of workspace wise_full_attn_accum_ws needs (0 for blocks 16 and 32)."""
+    d = WiseDesc(batch, heads, seq_len, head_dim, _block(block_size), 0.0)
+    n = load_library().wise_full_attn_accum_workspace_bytes(ctypes.byref(d))
+    if n < 0:
+        raise WiseError(WISE_ERR_INVALID_ARG, "wise_full_attn_accum_workspace_bytes", "invalid shape")
+    return int(n)
+
+
+def wise_full_attn_accum_ws(q, k, v, mass, block_size: int, o=None, workspace=None,
+                            softmax_scale: float = 0.0, stream=None):
+    """Discovery step as wise_full_attn_accum, with the block-mass partials
+    in a device workspace (a uint8 tensor of at least
+    wise_accum_workspace_bytes(...) bytes on the tensors' GPU; allocated here
+    when None).  Returns o."""
+    torch = _torch()
+    block_size = _block(block_size)
+    _qkv(q, k, v)
+    _need(mass, "mass", torch.float32, 4)
+    if tuple(mass.shape) != _mass_shape(q, block_size):
+        raise ValueError(f"mass must be {_mass_shape(q, block_size)}, got {tuple(mass.shape)}")
+    o = _out(o, q)
+    b, h, s, dh = q.shape
+    need = wise_accum_workspace_bytes(b, h, s, dh, block_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    named = [(q, "q"), (k, "k"), (v, "v"), (o, "o"), (mass, "mass")]
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1)
+        named.append((workspace, "workspace"))
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    dev = _same_device(*named)
+    d = _desc(q, block_size, softmax_scale, k)
+    _call("wise_full_attn_accum_ws", dev, stream, ctypes.byref(d), q.data_ptr(), k.data_ptr(),
+          v.data_ptr(), o.data_ptr(), mass.data_ptr(), ws_ptr, ws_bytes)
     return o
 
 

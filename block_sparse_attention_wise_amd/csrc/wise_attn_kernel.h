@@ -183,6 +183,7 @@ __host__ __device__ constexpr size_t attn_lds_need(int mode, int nblk) {
                                    DmaTile<D, KT, AttnShape<D, BLK, KT, RPW>::kThreads>::kStageBytes
                              : AttnShape<D, BLK, KT, RPW>::kTileLds) +
          (mode == kDenseMass ? (size_t)RPW * ((size_t)nblk * LPR * (BLK + 1) + BLK) * 4 : 0) +
+         (mode == kDenseMassWs ? (size_t)RPW * BLK * 4 : 0) +
          (mode == kMassTwoPass ? (size_t)RPW * LPR * nblk * LPR * (BLK / 32) * 4 : 0) +
          (mode == kSparse ? (size_t)RPW * LPR * ((nblk * LPR + 31) / 32) * 4 + ((size_t)nblk + 1) * 4 : 0);
 }
@@ -226,7 +227,7 @@ __device__ __forceinline__ void store_rows(uint16_t* dst, int tid,
 template <int D, int BLK, int KT, int MODE, bool MASKED>
 __device__ __forceinline__ float softmax_prep(float* part, float scale_log2, int rel, int g, int n,
                                              int wave, int kb, float& m_ref, float& l_part,
-                                             float& blk_part, float run_max,
+                                             float& blk_part, float run_max, int pstride,
                                              f32x16_t (&s)[AttnShape<D, BLK, KT>::kM],
                                              f32x16_t (&oacc)[AttnShape<D, BLK, KT>::kDTiles]) {
   using Sh = AttnShape<D, BLK, KT>;
@@ -261,10 +262,10 @@ __device__ __forceinline__ float softmax_prep(float* part, float scale_log2, int
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[t][i] *= f;
       l_part *= f;
-      if constexpr (MODE == kDenseMass) {
+      if constexpr (MODE == kDenseMass || MODE == kDenseMassWs) {
         blk_part *= f;
         if (g == 0 && f != 1.f)
-          for (int b = 0; b < kb; ++b) part[b * (BLK + 1) + wave * 32 + n] *= f;
+          for (int b = 0; b < kb; ++b) part[(size_t)b * pstride + wave * 32 + n] *= f;
       }
     }
     m_ref = m_new;
@@ -288,6 +289,8 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   static_assert(LPR == 1 || (LPR == 2 && BLK == 32 && KT == 32 && RPW <= 2 && MODE != kDense),
                 "logical sub-blocks: block 16 on 32 x 32 tiles, at most two rows per workgroup");
   static_assert(RPW * LPR * LPR <= 8, "list-entry tag bits");
+  static_assert(MODE != kDenseMassWs || (LPR == 1 && BLK >= 64), "workspace mass mode: blocks 64 and 128");
+  constexpr bool kMass1 = (MODE == kDenseMass || MODE == kDenseMassWs);   // one-pass block mass
 
   using Dm = DmaTile<D, KT, Sh::kThreads>;
   constexpr bool kDma = uses_dma<MODE>();
@@ -340,8 +343,18 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   const bool row_ok = qb < p.nblk;
   const int row = bh * p.nblk + qb;
 
+  // One-pass block mass: this wave's row of (query, key block) partials,
+  // [key block][query of the row] with stride pstride, and the queries'
+  // 1/l.  In LDS for kDenseMass (rows padded by one against bank
+  // conflicts); in the caller's workspace for kDenseMassWs, 1/l in LDS.
   float* part = reinterpret_cast<float*>(extra) + (size_t)slot * ((size_t)lnb * (BLK + 1) + BLK);
   float* invl = part + (size_t)lnb * (BLK + 1);                           // kDenseMass
+  int pstride = BLK + 1;
+  if constexpr (MODE == kDenseMassWs) {
+    part = p.work + (size_t)row * lnb * BLK;
+    invl = reinterpret_cast<float*>(extra) + (size_t)slot * BLK;
+    pstride = BLK;
+  }
   float* slots = reinterpret_cast<float*>(extra);   // kMassTwoPass: [RPW*LPR][lnb][BLK/32]
 
   const size_t head_off = (size_t)bh * p.seq * D;
@@ -573,10 +586,10 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
 
   // Causal mask (diagonal block only), lazy-rescale check and rare rescale.
   auto prep = [&]<bool MASKED>(int kb, int sub, f32x16_t (&sc)[Sh::kM]) __attribute__((always_inline)) {
-    constexpr bool kTrack = (MODE == kDenseMass || MODE == kMassTwoPass);
+    constexpr bool kTrack = (kMass1 || MODE == kMassTwoPass);
     return softmax_prep<D, BLK, KT, MODE, MASKED>(part, p.scale_log2, qrow - (kb * BLK + sub * KT), g, n, wr,
                                                   kb * LPR, m_ref, l_part, blk_part,
-                                                  kTrack ? m_hi : -INFINITY, sc, oacc);
+                                                  kTrack ? m_hi : -INFINITY, pstride, sc, oacc);
   };
 
   // P = exp2(s * scale*log2e - m) per 32-key sub-tile, then that
@@ -595,11 +608,11 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float pv = __builtin_amdgcn_exp2f(fmaf(sc[m][kk * 8 + e], p.scale_log2, neg_m));
-          if constexpr (MODE == kDenseMass) tsum += pv;   // block mass needs the fp32 values
+          if constexpr (kMass1) tsum += pv;   // block mass needs the fp32 values
           if constexpr (MODE == kDenseMass && LPR == 2) hsum[kk] += pv;
           pf[kk][e] = (__bf16)pv;
         }
-      if constexpr (MODE != kDenseMass) {
+      if constexpr (!kMass1) {
         // Row sum of the bf16 operands themselves (the same values the PV
         // product uses), two per packed dot product.  O is divided by this
         // sum: the weights then add up to one however P was rounded, so the
@@ -640,11 +653,11 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
         const float bp = hsum[kh] + __shfl_xor(hsum[kh], 32);
         if (g == 0) part[(kb * 2 + kh) * (BLK + 1) + n] = bp;
       }
-    } else if constexpr (MODE == kDenseMass) {
+    } else if constexpr (kMass1) {
       blk_part += tsum;
       if (sub == Sh::kSub - 1) {
         const float bp = blk_part + __shfl_xor(blk_part, 32);
-        if (g == 0) part[kb * (BLK + 1) + wr * 32 + n] = bp;
+        if (g == 0) part[(size_t)kb * pstride + wr * 32 + n] = bp;
         blk_part = 0.f;
       }
     }
@@ -670,7 +683,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
       }
     }
     const float run_max = prep.template operator()<MASKED>(kb, sub, sc);
-    if constexpr (MODE == kDenseMass) m_hi = run_max;
+    if constexpr (kMass1) m_hi = run_max;
     expv(kb, sub, sc, Vt);
   };
 
@@ -883,7 +896,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   // only with a score above this one.  (Lanes of a query that hold an equal
   // largest score each count theirs.)
   float lo = lt;
-  if constexpr (MODE == kDenseMass) {
+  if constexpr (kMass1) {
     const float mh = fmaxf(m_hi, __shfl_xor(m_hi, 32));
     float d = 0.f;
     if (mh != -INFINITY && m_hi == mh) {
@@ -947,6 +960,25 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
       float acc = 0.f;
       for (int i = lr * kLB; i < (lr + 1) * kLB; ++i) acc = fmaf(pr[i], il[i], acc);
       p.mass[((size_t)bh * lnb + lq) * lnb + b] += acc * (1.0f / kLB);
+    }
+  }
+  if constexpr (MODE == kDenseMassWs) {
+    if (row_ok && g == 0) invl[wr * 32 + n] = inv;
+    // The barrier (with its workgroup-scope fences) also makes every wave's
+    // partial stores to the workspace visible to the whole workgroup.
+    __syncthreads();
+    // Row slot r's masses: r_qb = (1/B) sum_i partial_ib / l_i, one
+    // sequential sum per key block (deterministic), the B partials of a
+    // block contiguous in the workspace.
+    for (int w = tid; w < RPW * lnb; w += Sh::kThreads) {
+      const int r = w / lnb, b = w % lnb;
+      const int qr = q_lo + r;
+      if (qr >= p.nblk || b > qr) continue;
+      const float* pr = p.work + ((size_t)(bh * p.nblk + qr) * lnb + b) * BLK;
+      const float* il = reinterpret_cast<const float*>(extra) + (size_t)r * BLK;
+      float acc = 0.f;
+      for (int i = 0; i < BLK; ++i) acc = fmaf(pr[i], il[i], acc);
+      p.mass[((size_t)bh * lnb + qr) * lnb + b] += acc * (1.0f / BLK);
     }
   }
 }
@@ -1145,6 +1177,9 @@ hipError_t launch_attn_blk(int mode_in, const AttnParams& p, hipStream_t stream)
     case kDense: return launch_cfg<D, BLK, kDense>(c, p, stream);
     case kSparse: return launch_cfg<D, BLK, kSparse>(c, p, stream);
     case kMassTwoPass: return launch_cfg<D, BLK, kMassTwoPass>(c, p, stream);
+    case kDenseMassWs:
+      if constexpr (BLK >= 64) return launch_cfg<D, BLK, kDenseMassWs>(c, p, stream);
+      else return hipErrorInvalidValue;
     default: return launch_cfg<D, BLK, kDenseMass>(c, p, stream);
   }
 }
@@ -1193,8 +1228,15 @@ size_t attn_lds_bytes_blk(int mode_in, int nblk) {
   return c.kt ? cfg_lds<D, BLK>(c.kt, c.rpw, mode, nblk) : 0;
 }
 
+// The workspace mass mode exists for blocks 64 and 128; smaller blocks run
+// the LDS mass launches (their partials are small).
+inline int mode_for_block(int block, int mode) {
+  return (mode == kDenseMassWs && block < 64) ? kDenseMass : mode;
+}
+
 template <int D>
-size_t attn_lds_bytes_d(int block, int mode, int nblk) {
+size_t attn_lds_bytes_d(int block, int mode_in, int nblk) {
+  const int mode = mode_for_block(block, mode_in);
   switch (block) {
     case 16: return attn_lds_bytes_b16<D>(mode, nblk);
     case 32: return attn_lds_bytes_blk<D, 32>(mode, nblk);
@@ -1205,7 +1247,8 @@ size_t attn_lds_bytes_d(int block, int mode, int nblk) {
 }
 
 template <int D>
-hipError_t launch_attn_d(int block, int mode, const AttnParams& p, hipStream_t stream) {
+hipError_t launch_attn_d(int block, int mode_in, const AttnParams& p, hipStream_t stream) {
+  const int mode = mode_for_block(block, mode_in);
   switch (block) {
     case 16: return launch_attn_b16<D>(mode, p, stream);
     case 32: return launch_attn_blk<D, 32>(mode, p, stream);

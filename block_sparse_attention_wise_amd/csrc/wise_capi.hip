@@ -93,7 +93,7 @@ float scale_log2(const wise_attn_desc_t* d) {
 
 wise_status_t run_attn(const wise_attn_desc_t* d, int mode, const void* q, const void* k, const void* v,
                        void* o, float* lse, float* mass, const int32_t* row_ptr, const int32_t* col_idx,
-                       void* stream) {
+                       void* stream, float* work = nullptr) {
   int32_t nblk;
   int64_t n_rows;
   wise_status_t st = check_desc(d, &nblk, &n_rows);
@@ -103,7 +103,8 @@ wise_status_t run_attn(const wise_attn_desc_t* d, int mode, const void* q, const
   if ((st = check_tensor(v, "v")) != WISE_OK) return st;
   if ((st = check_tensor(o, "o")) != WISE_OK) return st;
   if (o == q || o == k || o == v) return fail(WISE_ERR_INVALID_ARG, "o aliases an input");
-  if (mode == kDenseMass && mass == nullptr) return fail(WISE_ERR_INVALID_ARG, "mass is NULL");
+  if ((mode == kDenseMass || mode == kDenseMassWs) && mass == nullptr)
+    return fail(WISE_ERR_INVALID_ARG, "mass is NULL");
   if (mode == kSparse && (row_ptr == nullptr || col_idx == nullptr))
     return fail(WISE_ERR_INVALID_ARG, "row_ptr / col_idx is NULL");
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u))
@@ -132,10 +133,18 @@ wise_status_t run_attn(const wise_attn_desc_t* d, int mode, const void* q, const
   p.seq = d->seq_len;
   p.nblk = nblk;
   p.scale_log2 = scale_log2(d);
+  p.work = work;
   AttnLaunch cfg{d->head_dim, d->block_size, mode};
   const hipError_t e = launch_attn(cfg, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(WISE_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+// Workspace of the mass launch: one fp32 partial per (row, key block, query
+// of the row), for blocks 64 and 128; smaller blocks need none.
+int64_t accum_workspace_bytes(const wise_attn_desc_t* d, int32_t nblk, int64_t n_rows) {
+  if (d->block_size < 64) return 0;
+  return n_rows * (int64_t)nblk * d->block_size * 4;
 }
 
 int64_t max_nnz(int32_t nblk, int64_t heads_total, int32_t max_blocks) {
@@ -163,6 +172,34 @@ wise_status_t wise_full_attn(const wise_attn_desc_t* desc, const void* q, const 
 wise_status_t wise_full_attn_accum(const wise_attn_desc_t* desc, const void* q, const void* k,
                                    const void* v, void* o, float* mass, void* stream) {
   return run_attn(desc, kDenseMass, q, k, v, o, nullptr, mass, nullptr, nullptr, stream);
+}
+
+int64_t wise_full_attn_accum_workspace_bytes(const wise_attn_desc_t* desc) {
+  int32_t nblk;
+  int64_t n_rows;
+  if (check_desc(desc, &nblk, &n_rows) != WISE_OK) return -1;
+  return accum_workspace_bytes(desc, nblk, n_rows);
+}
+
+wise_status_t wise_full_attn_accum_ws(const wise_attn_desc_t* desc, const void* q, const void* k,
+                                      const void* v, void* o, float* mass, void* workspace,
+                                      int64_t workspace_bytes, void* stream) {
+  int32_t nblk;
+  int64_t n_rows;
+  wise_status_t st = check_desc(desc, &nblk, &n_rows);
+  if (st != WISE_OK) return st;
+  const int64_t need = accum_workspace_bytes(desc, nblk, n_rows);
+  if (need == 0) return run_attn(desc, kDenseMass, q, k, v, o, nullptr, mass, nullptr, nullptr, stream);
+  if (workspace == nullptr) return fail(WISE_ERR_INVALID_ARG, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) & 15u)
+    return fail(WISE_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(WISE_ERR_CAPACITY, "workspace_bytes %lld below the %lld this call needs",
+                (long long)workspace_bytes, (long long)need);
+  if (workspace == q || workspace == k || workspace == v || workspace == o || workspace == mass)
+    return fail(WISE_ERR_INVALID_ARG, "workspace aliases an input or output");
+  return run_attn(desc, kDenseMassWs, q, k, v, o, nullptr, mass, nullptr, nullptr, stream,
+                  static_cast<float*>(workspace));
 }
 
 wise_status_t wise_sparse_attn(const wise_attn_desc_t* desc, const void* q, const void* k, const void* v,

@@ -12,8 +12,10 @@ enum AttnMode : int {
   kDense = 0,       // Eq. (2) over every admissible key block
   kDenseMass = 1,   // Eq. (2) plus the block mass of Eq. (5), added into `mass`
   kSparse = 2,      // Eq. (8): only the key blocks listed in the CSR row
-  kMassTwoPass = 3  // kDenseMass in two passes over the keys (launcher's choice
+  kMassTwoPass = 3, // kDenseMass in two passes over the keys (launcher's choice
                     // for long rows): row max and sum first, then P, O and mass
+  kDenseMassWs = 4  // kDenseMass with the per-(query, key block) partials in a
+                    // caller's workspace in HBM instead of LDS (blocks 64, 128)
 };
 
 struct AttnParams {
@@ -32,6 +34,7 @@ struct AttnParams {
   int32_t nblk;            // seq / block
   float scale_log2;        // softmax scale * log2(e)
   int32_t head_chunk;      // workgroup order (set by the launcher): 0, or heads per chunk within an XCD
+  float* work;             // kDenseMassWs: partials [row][key block][query of the row]
 };
 
 struct AttnLaunch {

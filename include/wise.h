@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define WISE_ABI_VERSION 2
+#define WISE_ABI_VERSION 3
 
 typedef enum {
   WISE_OK = 0,
@@ -104,6 +104,33 @@ wise_status_t wise_full_attn(const wise_attn_desc_t* desc, const void* q, const 
  */
 wise_status_t wise_full_attn_accum(const wise_attn_desc_t* desc, const void* q, const void* k,
                                    const void* v, void* o, float* mass, void* stream);
+
+/*
+ * The discovery step of wise_full_attn_accum (the same Eq. 2 output and the
+ * same Section 5.1, Eq. (5) block mass, added into mass), with the
+ * per-(query, key block) partial sums of Eq. (5) kept in a caller-owned
+ * workspace in device memory instead of on chip.  For block sizes 64 and
+ * 128 this runs the mass launch at the dense kernel's tile size and
+ * occupancy at every sequence length, where wise_full_attn_accum has to
+ * shrink its tiles or walk the keys twice as rows grow.  For block sizes
+ * 16 and 32 the call is wise_full_attn_accum and the workspace is unused.
+ *
+ * q, k, v, o, mass: as in wise_full_attn_accum.
+ * workspace: device memory of at least
+ *       wise_full_attn_accum_workspace_bytes(desc) bytes, 16-byte aligned,
+ *       not overlapping any other argument (may be NULL when that size is
+ *       0).  Its contents on entry are ignored and on return unspecified:
+ *       it is scratch, and calls that share it must not overlap in time.
+ * workspace_bytes: its size; WISE_ERR_CAPACITY if it is too small.
+ */
+wise_status_t wise_full_attn_accum_ws(const wise_attn_desc_t* desc, const void* q, const void* k,
+                                      const void* v, void* o, float* mass, void* workspace,
+                                      int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes wise_full_attn_accum_ws needs for this descriptor:
+ * batch * heads * n_blocks^2 * block_size * 4 for block sizes 64 and 128,
+ * 0 for 16 and 32; -1 for an invalid descriptor. */
+int64_t wise_full_attn_accum_workspace_bytes(const wise_attn_desc_t* desc);
 
 /*
  * Working-set selection, Section 5.1, Eq. (6) (Appendix A.1, Eq. 12), once

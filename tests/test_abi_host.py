@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = _lib()
-    assert lib.wise_abi_version() == 2
+    assert lib.wise_abi_version() == 3
     assert lib.wise_status_string(0) == b"WISE_OK"
     assert lib.wise_status_string(3) == b"WISE_ERR_CAPACITY"
     assert lib.wise_status_string(99) == b"WISE_ERR_UNKNOWN"
@@ -127,7 +127,7 @@ def test_gqa_descriptor_rejected_when_heads_do_not_split():
         d.kv_heads = kv
         assert lib.wise_full_attn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None) \
             == wise.WISE_ERR_INVALID_ARG, kv
-    assert lib.wise_abi_version() == 2
+    assert lib.wise_abi_version() == 3
 
 
 def test_select_variant_arguments_rejected():
@@ -206,3 +206,26 @@ def test_m0_only_feeds_the_direct_lds_loads():
                 assert body[i + 1].startswith("buffer_load_dwordx4") and body[i + 1].endswith(" lds"), body[i + 1]
                 n_dma += 1
     assert n_dma > 0
+
+
+def test_accum_workspace_size_and_arguments():
+    lib = _lib()
+    for blk, nb in ((64, 8), (128, 4), (32, 8), (16, 16)):
+        d = _desc(b=2, h=3, s=blk * nb, d=64, blk=blk)
+        want = 2 * 3 * nb * nb * blk * 4 if blk >= 64 else 0
+        assert lib.wise_full_attn_accum_workspace_bytes(ctypes.byref(d)) == want
+        assert wise.wise_accum_workspace_bytes(2, 3, blk * nb, 64, blk) == want
+    assert lib.wise_full_attn_accum_workspace_bytes(None) == -1
+    d = _desc(s=512, blk=64)
+    need = lib.wise_full_attn_accum_workspace_bytes(ctypes.byref(d))
+    f = lib.wise_full_attn_accum_ws
+    O = FAKE + 65536
+    # no workspace, misaligned, too small, aliasing an argument: refused before any launch
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, O, FAKE + 4096, None, need, None) == wise.WISE_ERR_INVALID_ARG
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, O, FAKE + 4096, (FAKE << 8) + 4, need, None) \
+        == wise.WISE_ERR_INVALID_ARG
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, O, FAKE + 4096, FAKE << 8, need - 1, None) == wise.WISE_ERR_CAPACITY
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, O, FAKE + 4096, O, need, None) == wise.WISE_ERR_INVALID_ARG
+    # mass is still required
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, O, None, FAKE << 8, need, None) == wise.WISE_ERR_INVALID_ARG
+    assert lib.wise_last_error() != b""

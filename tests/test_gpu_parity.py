@@ -56,6 +56,15 @@ def _oracle_head(bits, b, h):
     return oracle.bf16_to_f64(bits[b, h])
 
 
+# The two entry points of the discovery step: block-mass partials on chip
+# (wise_full_attn_accum) or in a device workspace (wise_full_attn_accum_ws).
+ENTRIES = ["lds", "ws"]
+
+
+def _accum(entry):
+    return wise.wise_full_attn_accum if entry == "lds" else wise.wise_full_attn_accum_ws
+
+
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"b{s[0]}h{s[1]}s{s[2]}d{s[3]}B{s[4]}" for s in SHAPES])
 def test_dense_matches_oracle(shape):
     b_, h_, s_, d_, blk = shape
@@ -83,12 +92,13 @@ def test_dense_matches_oracle(shape):
             assert np.max(np.abs(lse_h[b, h] - ref_lse)) < 4e-3
 
 
+@pytest.mark.parametrize("entry", ENTRIES)
 @pytest.mark.parametrize("d_,blk", [(64, 32), (128, 64), (96, 128)])
-def test_dense_large_logits_rescale_path(d_, blk):
+def test_dense_large_logits_rescale_path(d_, blk, entry):
     """Logits spanning hundreds of units: the reference max jumps by more than
     the 64 log2-unit slack on about half of the non-first wave tiles, so the
     rescale of O, l and the mass partials runs many times."""
-    say(f"dense large logits d{d_} B{blk}")
+    say(f"dense large logits d{d_} B{blk} {entry}")
     s_ = 4 * blk
     g = np.random.default_rng(7)
     from wise_inputs import round_to_bf16_bits
@@ -98,7 +108,7 @@ def test_dense_large_logits_rescale_path(d_, blk):
     # later keys grow, so the max rises along the key walk
     o = wise.wise_full_attn(to_dev(q), to_dev(k), to_dev(v), blk, softmax_scale=1.0)
     mass = torch.zeros(1, 2, s_ // blk, s_ // blk, dtype=torch.float32, device="cuda")
-    o2 = wise.wise_full_attn_accum(to_dev(q), to_dev(k), to_dev(v), mass, blk, softmax_scale=1.0)
+    o2 = _accum(entry)(to_dev(q), to_dev(k), to_dev(v), mass, blk, softmax_scale=1.0)
     torch.cuda.synchronize()
     got, got2 = bf16_dev_to_f64(o), bf16_dev_to_f64(o2)
     mass_h = mass.cpu().numpy().astype(np.float64)
@@ -140,6 +150,8 @@ def test_peaked_rows_every_mode(shape):
     o = wise.wise_full_attn(qd, kd, vd, blk)
     mass = torch.zeros(1, h_, nb, nb, dtype=torch.float32, device="cuda")
     oa = wise.wise_full_attn_accum(qd, kd, vd, mass, blk)
+    mass_ws = torch.zeros_like(mass)
+    oa_ws = wise.wise_full_attn_accum_ws(qd, kd, vd, mass_ws, blk)
     # full causal support through the sparse kernel
     rows = [list(range(r % nb + 1)) for r in range(h_ * nb)]
     rp = np.zeros(len(rows) + 1, dtype=np.int32)
@@ -148,7 +160,9 @@ def test_peaked_rows_every_mode(shape):
     os_ = wise.wise_sparse_attn(qd, kd, vd, torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda(), blk)
     torch.cuda.synchronize()
     got, got_a, got_s = bf16_dev_to_f64(o), bf16_dev_to_f64(oa), bf16_dev_to_f64(os_)
+    got_w = bf16_dev_to_f64(oa_ws)
     mass_h = mass.cpu().numpy().astype(np.float64)
+    mass_w = mass_ws.cpu().numpy().astype(np.float64)
     sc = oracle.default_scale(d_)
     for h in range(h_):
         Q, K, V = (oracle.bf16_to_f64(x[0, h]) for x in (q, k, v))
@@ -156,15 +170,19 @@ def test_peaked_rows_every_mode(shape):
         compare_outputs(got[0, h], ref, f"O(dense) h{h}")
         compare_outputs(got_a[0, h], ref, f"O(accum) h{h}")
         compare_outputs(got_s[0, h], ref, f"O(sparse) h{h}")
+        compare_outputs(got_w[0, h], ref, f"O(accum, workspace) h{h}")
         # logits reach ~60 here; fp32 accumulation of the scores then moves
         # p by up to ~5e-4 relative in the worst case
-        assert np.max(np.abs(mass_h[0, h] - np.tril(oracle.block_mass(Q, K, sc, blk)))) < 1e-3
+        mref = np.tril(oracle.block_mass(Q, K, sc, blk))
+        assert np.max(np.abs(mass_h[0, h] - mref)) < 1e-3
+        assert np.max(np.abs(mass_w[0, h] - mref)) < 1e-3
 
 
+@pytest.mark.parametrize("entry", ENTRIES)
 @pytest.mark.parametrize("shape", SHAPES[:9], ids=[f"b{s[0]}h{s[1]}s{s[2]}d{s[3]}B{s[4]}" for s in SHAPES[:9]])
-def test_accum_mass_matches_oracle(shape):
+def test_accum_mass_matches_oracle(shape, entry):
     b_, h_, s_, d_, blk = shape
-    say(f"accum {shape}")
+    say(f"accum {shape} {entry}")
     steps = _steps(_cfg(*shape), 2)
     nb = s_ // blk
     mass = torch.zeros(b_, h_, nb, nb, dtype=torch.float32, device="cuda")
@@ -172,7 +190,7 @@ def test_accum_mass_matches_oracle(shape):
     dense_outs = []
     for _, q, k, v in steps:
         qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
-        outs.append(wise.wise_full_attn_accum(qd, kd, vd, mass, blk))
+        outs.append(_accum(entry)(qd, kd, vd, mass, blk))
         dense_outs.append(wise.wise_full_attn(qd, kd, vd, blk))
     torch.cuda.synchronize()
     mass_h = mass.cpu().numpy().astype(np.float64)
@@ -398,9 +416,10 @@ def test_small_trajectories_end_to_end():
             f"max-abs {stats['max_abs']:.2e}, mean-abs {np.mean(stats['mean_abs']):.2e}")
 
 
-# Long rows: the mass launch switches to its two-pass form (row max and sum
-# first, then normalised probabilities) when one-pass LDS partials would
-# leave too few resident waves.  (batch, heads, seq, head_dim, block)
+# Long rows: the on-chip mass launch switches to its two-pass form (row max
+# and sum first, then P, O and the mass) when one-pass LDS partials would
+# leave too few resident waves; the workspace launch keeps one pass with
+# its partials in device memory.  (batch, heads, seq, head_dim, block)
 LONG_SHAPES = [
     (1, 1, 32768, 128, 64),
     (1, 2, 8192, 64, 32),
@@ -408,17 +427,18 @@ LONG_SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("entry", ENTRIES)
 @pytest.mark.parametrize("shape", LONG_SHAPES, ids=[f"b{s[0]}h{s[1]}s{s[2]}d{s[3]}B{s[4]}" for s in LONG_SHAPES])
-def test_accum_long_rows_matches_oracle(shape):
+def test_accum_long_rows_matches_oracle(shape, entry):
     b_, h_, s_, d_, blk = shape
-    say(f"accum long rows {shape}")
+    say(f"accum long rows {shape} {entry}")
     steps = _steps(_cfg(*shape), 2)
     nb = s_ // blk
     mass = torch.zeros(b_, h_, nb, nb, dtype=torch.float32, device="cuda")
     qbs = sorted({0, 1, nb // 3, nb - 2, nb - 1})
     outs = []
     for _, q, k, v in steps:
-        o = wise.wise_full_attn_accum(to_dev(q), to_dev(k), to_dev(v), mass, blk)
+        o = _accum(entry)(to_dev(q), to_dev(k), to_dev(v), mass, blk)
         outs.append({qb: bf16_dev_to_f64(o[:, :, qb * blk:(qb + 1) * blk]) for qb in qbs})
     torch.cuda.synchronize()
     mass_h = mass.cpu().numpy().astype(np.float64)

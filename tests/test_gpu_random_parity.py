@@ -5,7 +5,8 @@ size (16, 32, 64, 128), 1-10 query blocks, 1-2 batches, 1-2 KV heads with
 1, 2 or 4 query heads each (grouped-query attention), the default or a
 random softmax scale, and Q and K at unit or 4x amplitude (4x makes rows
 whose softmax is dominated by one or two keys).  It runs the dense launch
-(with LSE), the mass launch and the sparse launch on messy CSR rows (empty,
+(with LSE), both mass launches (partials on chip and in a workspace) and
+the sparse launch on messy CSR rows (empty,
 the full causal row, random entries with repeats, entries outside [0, q]
 that the kernel must ignore, unsorted), and checks each against the fp64
 oracle: O to the output tolerance, the LSE to bf16-operand accuracy, the
@@ -84,10 +85,13 @@ def test_random_case(seed):
     o = wise.wise_full_attn(qd, kd, vd, blk, lse=lse, softmax_scale=c["scale"])
     mass = torch.zeros(b, h, nb, nb, dtype=torch.float32, device="cuda")
     oa = wise.wise_full_attn_accum(qd, kd, vd, mass, blk, softmax_scale=c["scale"])
+    mass_w = torch.zeros_like(mass)
+    ow = wise.wise_full_attn_accum_ws(qd, kd, vd, mass_w, blk, softmax_scale=c["scale"])
     osp = wise.wise_sparse_attn(qd, kd, vd, torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda(), blk,
                                 softmax_scale=c["scale"])
     torch.cuda.synchronize()
     got_o, got_a, got_s = bf16_dev_to_f64(o), bf16_dev_to_f64(oa), bf16_dev_to_f64(osp)
+    got_w, got_mass_w = bf16_dev_to_f64(ow), mass_w.cpu().numpy().astype(np.float64)
     got_lse, got_mass = lse.cpu().numpy().astype(np.float64), mass.cpu().numpy().astype(np.float64)
 
     sc = c["scale"] if c["scale"] > 0 else oracle.default_scale(d)
@@ -100,6 +104,7 @@ def test_random_case(seed):
             ref = oracle.dense_attention(Q, K, V, sc)
             compare_outputs(got_o[bb, hh], ref, f"dense O {tag}")
             compare_outputs(got_a[bb, hh], ref, f"mass-launch O {tag}")
+            compare_outputs(got_w[bb, hh], ref, f"workspace mass-launch O {tag}")
             # log-sum-exp of the scaled causal scores; the kernel's row sum adds
             # bf16-rounded probabilities (relative error <= 2^-8 each, so log(l)
             # moves by at most -log(1 - 2^-8) = 3.91e-3)
@@ -110,6 +115,7 @@ def test_random_case(seed):
             assert np.max(np.abs(got_lse[bb, hh] - ref_lse)) < 4e-3, f"lse {tag}"
             mref = np.tril(oracle.block_mass(Q, K, sc, blk))
             assert np.max(np.abs(got_mass[bb, hh] - mref)) <= mass_tolerance(1), f"mass {tag}"
+            assert np.max(np.abs(got_mass_w[bb, hh] - mref)) <= mass_tolerance(1), f"workspace mass {tag}"
             base = (bb * h + hh) * nb
             sups = {qb: sorted({x for x in rows[base + qb] if 0 <= x <= qb}) for qb in range(nb)}
             refs = oracle.masked_attention(Q, K, V, sups, blk, sc)
