@@ -49,6 +49,9 @@ def test_full_size_trajectory(name):
         f"B {cfg.block}, {n_steps} steps, {len(samples)} sampled rows")
     nb, B = cfg.n_blocks, cfg.block
     mass = torch.zeros(cfg.batch, cfg.heads, nb, nb, dtype=torch.float32, device="cuda")
+    # the discovery steps run as bench.py runs them: block-mass partials in a workspace
+    ws = torch.empty(max(wise.wise_accum_workspace_bytes(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, B), 16),
+                     dtype=torch.uint8, device="cuda")
     rows_idx = {(b, h, qb): (b, h, np.arange(qb * B, (qb + 1) * B)) for (b, h, qb) in samples}
     got = {}
     row_ptr = col_idx = None
@@ -56,7 +59,7 @@ def test_full_size_trajectory(name):
         qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
         del q, k, v
         if t < cfg.td:
-            o = wise.wise_full_attn_accum(qd, kd, vd, mass, B)
+            o = wise.wise_full_attn_accum_ws(qd, kd, vd, mass, B, workspace=ws)
         else:
             if row_ptr is None:
                 row_ptr, col_idx = wise.wise_select_support(mass, cfg.td, cfg.eta, cfg.head_dim, B, cfg.cap)
