@@ -30,8 +30,9 @@
 // reduction off the common path: with attention logits that keep growing
 // along the key walk, a slack of 8 rescaled on 43% of 64-key wave tiles,
 // 64 only on each wave's first tile.  The block mass of Eq. (5) reuses the same fp32 P:
-// each (query, key block) partial sum is stored in LDS relative to m and
-// normalised by the query's final row sum in the epilogue.
+// each (query, key block) partial sum is stored relative to m (in LDS, or
+// in a caller's workspace in device memory) and normalised by the query's
+// final row sum in the epilogue.
 #pragma once
 
 #include <algorithm>
