@@ -35,8 +35,11 @@ with their reasons in the design notes):
 3. The threshold test is inclusive (mass >= eta), in float64.
 4. Sink (block 0) and diagonal (block q) are added after the eta selection and
    do not count toward eta; the cap, if any, limits only the eta-ranked part.
-5. |I_q| = B for every block (sequence lengths are multiples of B); the
-   diagonal block's mass counts only admissible keys j <= i.
+5. Blocks are consecutive runs of B positions from position 0, so when S is
+   not a multiple of B the last block is shorter (n_blocks = ceil(S / B)).
+   |I_q| in Eq. (5) is the number of queries block q actually holds: B, or
+   S - (n_blocks - 1) B for a short last block.  The diagonal block's mass
+   counts only admissible keys j <= i.
 6. If rounding leaves the total admissible mass below eta, every admissible
    block is kept.
 7. Selection variants (Eq. (6) left / Eq. (18) temporal union; Appendix B
@@ -62,7 +65,7 @@ from typing import Dict, List, Optional, Sequence
 import numpy as np
 
 __all__ = [
-    "bf16_to_f64", "default_scale", "attention_weights", "attention_output",
+    "bf16_to_f64", "default_scale", "n_blocks", "block_rows", "attention_weights", "attention_output",
     "dense_attention", "block_mass", "block_mass_rows", "mean_block_mass",
     "select_support", "support_margins", "working_set_mask",
     "eta_support", "topk_support", "select_union", "select_static",
@@ -85,6 +88,16 @@ def default_scale(head_dim: int) -> float:
 
 def _rows(S: int, rows) -> np.ndarray:
     return np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+
+
+def n_blocks(S: int, block: int) -> int:
+    """Number of blocks of a length-S sequence, the last one possibly short (reading 5)."""
+    return -(-S // block)
+
+
+def block_rows(qb: int, block: int, S: int) -> np.ndarray:
+    """Positions I_q of block qb: qb*B .. min(S, (qb+1)*B) - 1 (reading 5)."""
+    return np.arange(qb * block, min(S, (qb + 1) * block))
 
 
 def _softmax_rows(s: np.ndarray) -> np.ndarray:
@@ -123,26 +136,30 @@ def dense_attention(q, k, v, scale: Optional[float] = None, rows=None) -> np.nda
 def block_mass_rows(a_q, block: int) -> np.ndarray:
     """Eq. (5) for one query block: r_qb for every key block b.
 
-    ``a_q`` holds the B rows of A belonging to query block q ([B, S]); the
-    result has S/B entries, r_qb = (1/B) sum_{i in I_q} sum_{j in I_b} A_ij.
+    ``a_q`` holds the |I_q| rows of A belonging to query block q
+    ([|I_q|, S]); the result has n_blocks entries,
+    r_qb = (1/|I_q|) sum_{i in I_q} sum_{j in I_b} A_ij.
     """
     B = block
-    nb = a_q.shape[1] // B
-    per_row_block = a_q.reshape(a_q.shape[0], nb, B).sum(axis=2)   # sum over j in I_b
-    return per_row_block.sum(axis=0) / a_q.shape[0]                 # (1/|I_q|) sum over i in I_q
+    S = a_q.shape[1]
+    nb = n_blocks(S, B)
+    padded = np.zeros((a_q.shape[0], nb * B))
+    padded[:, :S] = a_q                                              # a short last key block
+    per_row_block = padded.reshape(a_q.shape[0], nb, B).sum(axis=2)  # sum over j in I_b
+    return per_row_block.sum(axis=0) / a_q.shape[0]                  # (1/|I_q|) sum over i in I_q
 
 
 def block_mass(q, k, scale: float, block: int, qblocks=None) -> np.ndarray:
     """Block-mass matrix r[q, b] of one (batch, head) at one step, Eq. (5).
 
-    Returns [len(qblocks), S/B] (all query blocks by default).
+    Returns [len(qblocks), n_blocks] (all query blocks by default).
     """
     S = k.shape[0]
-    nb = S // block
+    nb = n_blocks(S, block)
     qbs = range(nb) if qblocks is None else qblocks
     out = []
     for qb in qbs:
-        rows = np.arange(qb * block, (qb + 1) * block)
+        rows = block_rows(qb, block, S)
         out.append(block_mass_rows(attention_weights(q, k, scale, rows), block))
     return np.array(out)
 
@@ -293,9 +310,9 @@ def jaccard(rows_a: Sequence[Sequence[int]], rows_b: Sequence[Sequence[int]]) ->
 
 def working_set_mask(support_row: Sequence[int], S: int, block: int, rows) -> np.ndarray:
     """Eq. (7) restricted to query rows in one query block: 0 if b(j) in W, else -inf."""
-    keep = np.zeros(S // block, dtype=bool)
+    keep = np.zeros(n_blocks(S, block), dtype=bool)
     keep[list(support_row)] = True
-    allowed = np.repeat(keep, block)                  # b(j) in W_{q(i)}
+    allowed = np.repeat(keep, block)[:S]              # b(j) in W_{q(i)}
     R = np.where(allowed, 0.0, -np.inf)
     return np.broadcast_to(R, (len(rows), S))
 
@@ -348,14 +365,16 @@ def trajectory_head(steps_qkv, td: int, block: int, eta: float, cap: int = 0,
     for t, (q, k, v) in enumerate(steps_qkv):
         S, D = q.shape
         sc = default_scale(D) if scale is None else scale
-        nb = S // block
+        nb = n_blocks(S, block)
         if qbs is None:
             qbs = list(range(nb)) if qblocks is None else [int(x) for x in qblocks]
-        rows = np.concatenate([np.arange(qb * block, (qb + 1) * block) for qb in qbs])
+        per_block = [block_rows(qb, block, S) for qb in qbs]
+        rows = np.concatenate(per_block)
         if t < td:
             a = attention_weights(q, k, sc, rows)
-            masses.append(np.array([block_mass_rows(a[i * block:(i + 1) * block], block)
-                                    for i in range(len(qbs))]))
+            ends = np.cumsum([len(r) for r in per_block])
+            masses.append(np.array([block_mass_rows(a[e - len(r):e], block)
+                                    for r, e in zip(per_block, ends)]))
             outputs.append(attention_output(a, v) if out_rows else None)
         else:
             if not supports:

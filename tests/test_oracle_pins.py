@@ -421,6 +421,57 @@ def pin_rolling_and_jaccard(impl):
     assert impl.jaccard([[1, 2]], [[3]]) == 0.0
 
 
+def pin_short_last_block_mass(impl):
+    """S not a multiple of B: the last block holds S - (nB - 1) B queries and
+    keys.  Q = 0 gives r_qb = (1/|I_q|) sum_{i in I_q} |{j in I_b : j <= i}| / (i + 1)
+    with |I_q| counted from the block's real extent, and every row of r,
+    the short one included, sums to one."""
+    S, D, B = 45, 4, 8
+    nb = 6                                   # blocks [0,8) ... [40,45)
+    _, k, _ = _rand(31, S, D)
+    a = impl.attention_weights(np.zeros((S, D)), k, 1.0)
+    for qb in range(nb):
+        lo, hi = qb * B, min(S, qb * B + B)
+        r = impl.block_mass_rows(a[lo:hi], B)
+        assert r.shape == (nb,)
+        expect = np.zeros(nb)
+        for i in range(lo, hi):
+            for b in range(nb):
+                n_adm = max(0, min(i, b * B + B - 1, S - 1) - b * B + 1)
+                expect[b] += n_adm / (i + 1)
+        np.testing.assert_allclose(r, expect / (hi - lo), rtol=0, atol=1e-14)
+    q, k, _ = _rand(32, S, D)
+    a = impl.attention_weights(q, k, 0.7)
+    for qb in range(nb):
+        r = impl.block_mass_rows(a[qb * B:min(S, qb * B + B)], B)
+        assert abs(r.sum() - 1.0) < 1e-13 and np.all(r[qb + 1:] == 0.0)
+
+
+def pin_short_last_block_prefix(impl):
+    """Causality: positions past S never reach the first S queries.  A
+    length-S problem (S not a multiple of B) therefore matches the first S
+    rows of a longer one that extends it to whole blocks: weights, the masses
+    of the whole query blocks, and late-step attention on any support."""
+    S, L, D, B = 53, 64, 6, 16
+    q, k, _ = _rand(33, L, D)
+    a_s = impl.attention_weights(q[:S], k[:S], 0.5)
+    a_l = impl.attention_weights(q, k, 0.5)
+    np.testing.assert_allclose(a_s, a_l[:S, :S], rtol=0, atol=1e-15)
+    assert np.all(a_l[:S, S:] == 0.0)
+    for qb in range(S // B):
+        rows = slice(qb * B, qb * B + B)
+        np.testing.assert_allclose(impl.block_mass_rows(a_s[rows], B),
+                                   impl.block_mass_rows(a_l[rows], B), rtol=0, atol=1e-15)
+    g = np.random.default_rng(34)
+    sup = {qb: sorted({0, qb} | set(g.integers(0, qb + 1, 2).tolist())) for qb in range(L // B)}
+    m_s = impl.masked_attention_weights(q[:S], k[:S], 0.5, B, sup, np.arange(S))
+    m_l = impl.masked_attention_weights(q, k, 0.5, B, sup, np.arange(L))
+    np.testing.assert_allclose(m_s, m_l[:S, :S], rtol=0, atol=1e-15)
+    full = {qb: list(range(qb + 1)) for qb in range(-(-S // B))}
+    assert np.max(np.abs(impl.masked_attention_weights(q[:S], k[:S], 0.5, B, full, np.arange(S))
+                         - a_s)) <= 1e-15
+
+
 PINS = [pin_uniform_when_q_zero, pin_constant_values, pin_single_position,
         pin_logistic_two_keys, pin_causal_rows_sum_to_one, pin_key_shift_invariance,
         pin_scale_is_a_temperature, pin_golden_dense, pin_block_mass_sums_to_one,
@@ -431,7 +482,8 @@ PINS = [pin_uniform_when_q_zero, pin_constant_values, pin_single_position,
         pin_full_support_reproduces_dense, pin_diagonal_only_support,
         pin_sink_and_diagonal_support, pin_masked_rows_normalised,
         pin_variants_golden, pin_eta_support_brute_force, pin_union_structure,
-        pin_matched_controls, pin_retained_mass, pin_rolling_and_jaccard]
+        pin_matched_controls, pin_retained_mass, pin_rolling_and_jaccard,
+        pin_short_last_block_mass, pin_short_last_block_prefix]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -463,8 +515,9 @@ def test_trajectory_dense_only_equals_dense():
         assert out["mass_sum"].shape == (S // B, S // B)
 
 
-def test_trajectory_eta_one_late_equals_dense():
-    S, D, B = 64, 8, 16
+@pytest.mark.parametrize("S", [64, 61])
+def test_trajectory_eta_one_late_equals_dense(S):
+    D, B = 8, 16
     steps = [_rand(40 + t, S, D) for t in range(4)]
     out = oracle.trajectory_head(steps, td=2, block=B, eta=1.0)
     for qb, sup in out["supports"].items():
@@ -473,6 +526,7 @@ def test_trajectory_eta_one_late_equals_dense():
         q, k, v = steps[t]
         assert np.max(np.abs(out["outputs"][t] - oracle.dense_attention(q, k, v))) <= 1e-15
     row_sums = out["mass_sum"].sum(axis=1)
+    assert out["mass_sum"].shape == (4, 4)
     np.testing.assert_allclose(row_sums, 2.0, rtol=0, atol=1e-13)
 
 
@@ -532,6 +586,10 @@ def _mut_mask_off_by_one(q, k, scale, rows=None):
 
 def _mut_mass_no_norm(a_q, block):
     return oracle.block_mass_rows(a_q, block) * a_q.shape[0]
+
+
+def _mut_mass_divides_by_block(a_q, block):
+    return oracle.block_mass_rows(a_q, block) * a_q.shape[0] / block
 
 
 def _mut_mass_wrong_axis(a_q, block):
@@ -654,6 +712,7 @@ MUTANTS = {
     "causal_off_by_one": dict(attention_weights=_mut_mask_off_by_one),
     "mass_missing_1_over_B": dict(block_mass_rows=_mut_mass_no_norm),
     "mass_wrong_axis": dict(block_mass_rows=_mut_mass_wrong_axis),
+    "mass_short_block_over_B": dict(block_mass_rows=_mut_mass_divides_by_block),
     "select_exclusive_threshold": dict(select_support=_mut_select_exclusive),
     "select_tie_to_higher_index": dict(select_support=_mut_select_tie_high),
     "select_one_block_short": dict(select_support=_mut_select_one_short),
