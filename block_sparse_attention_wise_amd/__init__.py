@@ -11,7 +11,7 @@ there is no fallback path.  Build the library with
 Layouts (see the header for the full contract):
   q, o         bf16  [batch, heads, seq_len, head_dim], contiguous, on the GPU
   k, v         bf16  [batch, kv_heads, seq_len, head_dim] (kv_heads divides heads)
-  mass         fp32  [batch, heads, n_blocks, n_blocks]
+  mass         fp32  [batch, heads, n_blocks, n_blocks], n_blocks = ceil(seq_len / block_size)
   row_ptr      int32 [batch * heads * n_blocks + 1]
   col_idx      int32 [>= wise_select_max_nnz(...)]
 """
@@ -210,7 +210,7 @@ def wise_full_attn(q, k, v, block_size: int, o=None, lse=None, softmax_scale: fl
 
 def _mass_shape(q, block_size):
     b, h, s, _ = q.shape
-    nb = s // block_size
+    nb = -(-s // block_size)          # the last block is short when s % block_size != 0
     return (b, h, nb, nb)
 
 
@@ -396,7 +396,7 @@ def wise_sparse_attn(q, k, v, row_ptr, col_idx, block_size: int, o=None,
     _need(row_ptr, "row_ptr", torch.int32, 1)
     _need(col_idx, "col_idx", torch.int32, 1)
     b, h, s, _ = q.shape
-    if row_ptr.numel() != b * h * (s // block_size) + 1:
+    if row_ptr.numel() != b * h * -(-s // block_size) + 1:
         raise ValueError("row_ptr must have batch*heads*n_blocks + 1 entries")
     o = _out(o, q)
     dev = _same_device((q, "q"), (k, "k"), (v, "v"), (o, "o"), (row_ptr, "row_ptr"), (col_idx, "col_idx"))

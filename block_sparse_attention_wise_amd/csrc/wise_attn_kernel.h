@@ -203,6 +203,23 @@ __device__ __forceinline__ void load_rows(__amdgpu_buffer_rsrc_t rs, int key0, i
   }
 }
 
+// load_rows for a tile that reaches past the end of the sequence: `rs`
+// starts at the tile's first in-range row and every lane's offset is
+// clamped to `lim`, the last in-range 16 bytes, so no lane reads outside
+// the tensor (the rows past the end receive copies of in-range data).
+template <int D, int BLK, int KT, int RPW>
+__device__ __forceinline__ void load_rows_clamped(__amdgpu_buffer_rsrc_t rs, int lim, int tid,
+                                                  u32x4_t (&reg)[AttnShape<D, BLK, KT, RPW>::kPer]) {
+  using Sh = AttnShape<D, BLK, KT, RPW>;
+  constexpr int NT = Sh::kThreads;
+#pragma unroll
+  for (int i = 0; i < Sh::kPer; ++i) {
+    const int u = tid + i * NT;
+    if (Sh::kUnits % NT == 0 || u < Sh::kUnits)
+      reg[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, min(u * 16, lim), 0, 0));
+  }
+}
+
 // VGPR -> LDS, row-major with padded rows of STRIDE u16.
 template <int D, int BLK, int KT, int RPW, int STRIDE>
 __device__ __forceinline__ void store_rows(uint16_t* dst, int tid,
@@ -366,12 +383,16 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   const uint16_t* Kh = p.k + kv_off;
   const uint16_t* Vh = p.v + kv_off;
   const int qrow = qb * BLK + wr * 32 + n;
+  // When seq_len is not a multiple of the block size the last query block
+  // is short: its queries past the end are computed on zero Q, and neither
+  // stored nor counted in the block mass.
+  const bool q_ok = row_ok && qrow < p.seq;
 
   bf16x8_t qf[Sh::kChunks];
 #pragma unroll
   for (int c = 0; c < Sh::kChunks; ++c)
-    qf[c] = row_ok ? *reinterpret_cast<const bf16x8_t*>(Qh + (size_t)qrow * D + c * 16 + 8 * g)
-                   : bf16x8_t{};
+    qf[c] = q_ok ? *reinterpret_cast<const bf16x8_t*>(Qh + (size_t)qrow * D + c * 16 + 8 * g)
+                 : bf16x8_t{};
 
   const int head_bytes = p.seq * D * 2;
   // Direct-to-LDS staging (dense and sparse): per-lane read offsets into a
@@ -403,7 +424,32 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
   const i32x4_t kdesc = buffer_desc(Kh, (uint32_t)head_bytes);
   const i32x4_t vdesc = buffer_desc(Vh, (uint32_t)head_bytes);
+  // A tile that reaches past the end of the sequence (only in the last key
+  // block, when seq_len is not a multiple of the block size) is read
+  // through a resource that starts at its first in-range row (row seq-1 for
+  // a tile wholly past the end), with every lane's offset clamped to the
+  // last in-range 16 bytes: no lane reads outside the tensor, and the rows
+  // past the end receive copies of in-range data.  Their keys come after
+  // every real query of the only row that lists the block, its diagonal
+  // one, so the causal mask removes them.
+  auto dma_part = [&](int stage, int key0, bool with_v) __attribute__((always_inline)) {
+    const int r0 = min(key0, p.seq - 1);
+    const uint32_t bytes = (uint32_t)(p.seq - r0) * D * 2;
+    const uint32_t lim = bytes - 16;
+    const i32x4_t kd = buffer_desc(Kh + (size_t)r0 * D, bytes);
+    const i32x4_t vd = buffer_desc(Vh + (size_t)r0 * D, bytes);
+    const uint32_t kbase = __builtin_amdgcn_readfirstlane(lds0 + stage * Dm::kStageBytes + wave_u * 1024);
+#pragma unroll
+    for (int i = 0; i < Dm::kInstr; ++i) {
+      dma16(kd, kbase + i * Dm::kWaves * 1024, min(dk[i], lim), 0);
+      if (with_v) dma16(vd, kbase + i * Dm::kWaves * 1024 + Dm::kTileBytes, min(dv[i], lim), 0);
+    }
+  };
   auto dma_tile = [&](int stage, int key0) __attribute__((always_inline)) {
+    if (key0 + KT > p.seq) {
+      dma_part(stage, key0, true);
+      return;
+    }
     const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)key0 * D * 2);
     const uint32_t kbase = __builtin_amdgcn_readfirstlane(lds0 + stage * Dm::kStageBytes + wave_u * 1024);
 #pragma unroll
@@ -414,6 +460,10 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   };
   // K half only (first pass of the two-pass mass mode).
   auto dma_k = [&](int stage, int key0) __attribute__((always_inline)) {
+    if (key0 + KT > p.seq) {
+      dma_part(stage, key0, false);
+      return;
+    }
     const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)key0 * D * 2);
     const uint32_t kbase = __builtin_amdgcn_readfirstlane(lds0 + stage * Dm::kStageBytes + wave_u * 1024);
 #pragma unroll
@@ -580,9 +630,6 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
         }
       }
     }
-  };
-  auto scores = [&](f32x16_t (&sc)[Sh::kM], const uint16_t* Kt) __attribute__((always_inline)) {
-    scores_l.template operator()<0>(sc, Kt, 0, 0);
   };
 
   // Causal mask (diagonal block only), lazy-rescale check and rare rescale.
@@ -789,14 +836,15 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
       lds_barrier();
       const uint16_t* Kt = reinterpret_cast<const uint16_t*>(smem + st * Dm::kStageBytes);
       const int nkey0 = it + 1 < n_tiles ? tile_key0(it + 1) : -1;
-      if (mine && nkey0 >= 0) {
+      if (mine && nkey0 >= 0 && nkey0 + KT <= p.seq) {
         if (kb == qb) sum_tile.template operator()<true, true>(kb, sub, Kt, st ^ 1, nkey0);
         else sum_tile.template operator()<false, true>(kb, sub, Kt, st ^ 1, nkey0);
-      } else if (mine) {
-        if (kb == qb) sum_tile.template operator()<true>(kb, sub, Kt);
-        else sum_tile.template operator()<false>(kb, sub, Kt);
-      } else if (nkey0 >= 0) {
-        dma_k(st ^ 1, nkey0);
+      } else {
+        if (nkey0 >= 0) dma_k(st ^ 1, nkey0);
+        if (mine) {
+          if (kb == qb) sum_tile.template operator()<true>(kb, sub, Kt);
+          else sum_tile.template operator()<false>(kb, sub, Kt);
+        }
       }
     }
     // Bring the row sum from the lazy reference to the exact max.
@@ -804,7 +852,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
     const float m_ex = mh * p.scale_log2;
     l_two = (mh == -INFINITY) ? 0.f
                               : (l_part + __shfl_xor(l_part, 32)) * __builtin_amdgcn_exp2f(m_ref - m_ex);
-    const float inv_l = l_two > 0.f ? 1.f / l_two : 0.f;
+    const float inv_l = (l_two > 0.f && q_ok) ? 1.f / l_two : 0.f;   // padded queries add no mass
     const float neg_m = (mh == -INFINITY) ? 0.f : -m_ex;
     // Second pass over the same tiles with K and V.
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -821,14 +869,15 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
       const uint16_t* Kt = reinterpret_cast<const uint16_t*>(smem + st * Dm::kStageBytes);
       const uint16_t* Vt = Kt + KT * D;
       const int nkey0 = it + 1 < n_tiles ? tile_key0(it + 1) : -1;
-      if (mine && nkey0 >= 0) {
+      if (mine && nkey0 >= 0 && nkey0 + KT <= p.seq) {
         if (kb == qb) mass_tile.template operator()<true, true>(kb, sub, Kt, Vt, neg_m, inv_l, st ^ 1, nkey0);
         else mass_tile.template operator()<false, true>(kb, sub, Kt, Vt, neg_m, inv_l, st ^ 1, nkey0);
-      } else if (mine) {
-        if (kb == qb) mass_tile.template operator()<true>(kb, sub, Kt, Vt, neg_m, inv_l);
-        else mass_tile.template operator()<false>(kb, sub, Kt, Vt, neg_m, inv_l);
-      } else if (nkey0 >= 0) {
-        dma_tile(st ^ 1, nkey0);
+      } else {
+        if (nkey0 >= 0) dma_tile(st ^ 1, nkey0);
+        if (mine) {
+          if (kb == qb) mass_tile.template operator()<true>(kb, sub, Kt, Vt, neg_m, inv_l);
+          else mass_tile.template operator()<false>(kb, sub, Kt, Vt, neg_m, inv_l);
+        }
       }
     }
   } else if constexpr (kDma) {
@@ -848,23 +897,39 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
       const uint16_t* Kt = reinterpret_cast<const uint16_t*>(smem + st * Dm::kStageBytes);
       const uint16_t* Vt = Kt + KT * D;
       // The next tile's loads ride along with this tile's QK^T MFMAs when
-      // this wave computes; a wave with nothing to compute issues them at once.
+      // this wave computes; a wave with nothing to compute issues them at
+      // once, and so does every wave for a tile past the sequence end.
       const int nkey0 = it + 1 < n_tiles ? tile_key0(it + 1) : -1;
-      if (mine && nkey0 >= 0) {
+      if (mine && nkey0 >= 0 && nkey0 + KT <= p.seq) {
         if (kb == qb) compute_tile.template operator()<true, true>(kb, sub, Kt, Vt, pairs, st ^ 1, nkey0);
         else compute_tile.template operator()<false, true>(kb, sub, Kt, Vt, pairs, st ^ 1, nkey0);
-      } else if (mine) {
-        if (kb == qb) compute_tile.template operator()<true>(kb, sub, Kt, Vt, pairs);
-        else compute_tile.template operator()<false>(kb, sub, Kt, Vt, pairs);
-      } else if (nkey0 >= 0) {
-        dma_tile(st ^ 1, nkey0);
+      } else {
+        if (nkey0 >= 0) dma_tile(st ^ 1, nkey0);
+        if (mine) {
+          if (kb == qb) compute_tile.template operator()<true>(kb, sub, Kt, Vt, pairs);
+          else compute_tile.template operator()<false>(kb, sub, Kt, Vt, pairs);
+        }
       }
     }
   } else {
-  if (n_tiles > 0) {
-    load_rows<D, BLK, KT, RPW>(krs, tile_key0(0), tid, kreg);
-    load_rows<D, BLK, KT, RPW>(vrs, tile_key0(0), tid, vreg);
-  }
+  // K/V of one tile into registers (clamped past the sequence end, as for
+  // the direct-to-LDS loads).
+  auto load_kv = [&](int key0) __attribute__((always_inline)) {
+    if (key0 + KT <= p.seq) {
+      load_rows<D, BLK, KT, RPW>(krs, key0, tid, kreg);
+      load_rows<D, BLK, KT, RPW>(vrs, key0, tid, vreg);
+    } else {
+      const int r0 = min(key0, p.seq - 1);
+      const int bytes = (p.seq - r0) * D * 2;
+      load_rows_clamped<D, BLK, KT, RPW>(
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Kh + (size_t)r0 * D), 0, bytes, 0x00020000),
+          bytes - 16, tid, kreg);
+      load_rows_clamped<D, BLK, KT, RPW>(
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Vh + (size_t)r0 * D), 0, bytes, 0x00020000),
+          bytes - 16, tid, vreg);
+    }
+  };
+  if (n_tiles > 0) load_kv(tile_key0(0));
   for (int it = 0; it < n_tiles; ++it) {
     int kb;
     bool mine;
@@ -874,11 +939,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
     store_rows<D, BLK, KT, RPW, Sh::kKsStride>(Ks, tid, kreg);
     store_rows<D, BLK, KT, RPW, Sh::kVStride>(Vs, tid, vreg);
     __syncthreads();
-    if (it + 1 < n_tiles) {
-      const int nk = tile_key0(it + 1);
-      load_rows<D, BLK, KT, RPW>(krs, nk, tid, kreg);
-      load_rows<D, BLK, KT, RPW>(vrs, nk, tid, vreg);
-    }
+    if (it + 1 < n_tiles) load_kv(tile_key0(it + 1));
     if (mine) {
       if (kb == qb) compute_tile.template operator()<true>(kb, sub, Ks, Vs, 0xFu);
       else compute_tile.template operator()<false>(kb, sub, Ks, Vs, 0xFu);
@@ -907,7 +968,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
     lo = lt + (d + __shfl_xor(d, 32));
   }
   const float inv_o = lo > 0.f ? 1.f / lo : 0.f;
-  if (row_ok) {
+  if (q_ok) {
     uint16_t* Oh = p.o + head_off + (size_t)qrow * D;
 #pragma unroll
     for (int t = 0; t < Sh::kDTiles; ++t)
@@ -928,9 +989,15 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
     }
   }
 
+  // |I_q| of Eq. (5): the block's query count, short for the last block
+  // when seq_len is not a multiple of the block size.
+  auto mass_div = [&](float acc, int lq) __attribute__((always_inline)) {
+    const int cnt = min(kLB, p.seq - lq * kLB);
+    return cnt == kLB ? acc * (1.0f / kLB) : acc / (float)cnt;
+  };
   if constexpr (MODE == kMassTwoPass) {
     lds_barrier();
-    // r_qb = (1/B) * (sum of the logical row's wave slots, in wave order).
+    // r_qb = (1/|I_q|) * (sum of the logical row's wave slots, in wave order).
     for (int w = tid; w < RPW * LPR * lnb; w += Sh::kThreads) {
       const int rl = w / lnb, b = w % lnb;
       const int qphys = q_lo + rl / LPR;
@@ -940,13 +1007,13 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
       float acc = 0.f;
 #pragma unroll
       for (int i = 0; i < WR; ++i) acc += slots[(rl * lnb + b) * WR + i];
-      p.mass[((size_t)bh * lnb + lq) * lnb + b] += acc * (1.0f / kLB);
+      p.mass[((size_t)bh * lnb + lq) * lnb + b] += mass_div(acc, lq);
     }
   }
   if constexpr (MODE == kDenseMass) {
-    if (row_ok && g == 0) invl[wr * 32 + n] = inv;
+    if (row_ok && g == 0) invl[wr * 32 + n] = q_ok ? inv : 0.f;   // padded queries add no mass
     __syncthreads();
-    // Row slot r's masses: r_qb = (1/B) sum_i partial_ib / l_i, one
+    // Row slot r's masses: r_qb = (1/|I_q|) sum_i partial_ib / l_i, one
     // sequential sum per key block (deterministic).
     for (int w = tid; w < RPW * LPR * lnb; w += Sh::kThreads) {
       const int rl = w / lnb, b = w % lnb;
@@ -960,15 +1027,15 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
       pr += b * (BLK + 1);
       float acc = 0.f;
       for (int i = lr * kLB; i < (lr + 1) * kLB; ++i) acc = fmaf(pr[i], il[i], acc);
-      p.mass[((size_t)bh * lnb + lq) * lnb + b] += acc * (1.0f / kLB);
+      p.mass[((size_t)bh * lnb + lq) * lnb + b] += mass_div(acc, lq);
     }
   }
   if constexpr (MODE == kDenseMassWs) {
-    if (row_ok && g == 0) invl[wr * 32 + n] = inv;
+    if (row_ok && g == 0) invl[wr * 32 + n] = q_ok ? inv : 0.f;
     // The barrier (with its workgroup-scope fences) also makes every wave's
     // partial stores to the workspace visible to the whole workgroup.
     __syncthreads();
-    // Row slot r's masses: r_qb = (1/B) sum_i partial_ib / l_i, one
+    // Row slot r's masses: r_qb = (1/|I_q|) sum_i partial_ib / l_i, one
     // sequential sum per key block (deterministic), the B partials of a
     // block contiguous in the workspace.
     for (int w = tid; w < RPW * lnb; w += Sh::kThreads) {
@@ -979,7 +1046,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
       const float* il = reinterpret_cast<const float*>(extra) + (size_t)r * BLK;
       float acc = 0.f;
       for (int i = 0; i < BLK; ++i) acc = fmaf(pr[i], il[i], acc);
-      p.mass[((size_t)bh * lnb + qr) * lnb + b] += acc * (1.0f / BLK);
+      p.mass[((size_t)bh * lnb + qr) * lnb + b] += mass_div(acc, qr);
     }
   }
 }

@@ -62,20 +62,20 @@ wise_status_t check_desc(const wise_attn_desc_t* d, int32_t* nblk, int64_t* n_ro
     return fail(WISE_ERR_UNSUPPORTED, "block_size %d not built (16, 32, 64, 128)", d->block_size);
   if (d->head_dim != 64 && d->head_dim != 96 && d->head_dim != 128)
     return fail(WISE_ERR_UNSUPPORTED, "head_dim %d not built (64, 96, 128)", d->head_dim);
-  if (d->seq_len < d->block_size || d->seq_len % d->block_size != 0)
-    return fail(WISE_ERR_INVALID_ARG, "seq_len %d must be a positive multiple of block_size %d",
-                d->seq_len, d->block_size);
+  if (d->seq_len < 1) return fail(WISE_ERR_INVALID_ARG, "seq_len %d must be >= 1", d->seq_len);
   if (d->seq_len > 65536)
     return fail(WISE_ERR_UNSUPPORTED, "seq_len %d above 65536", d->seq_len);
   if (!std::isfinite(d->softmax_scale))
     return fail(WISE_ERR_INVALID_ARG, "softmax_scale is not finite");
   if (d->kv_heads < 0 || (d->kv_heads > 0 && d->heads % d->kv_heads != 0))
     return fail(WISE_ERR_INVALID_ARG, "kv_heads %d must be 0 or divide heads %d", d->kv_heads, d->heads);
+  // The last block is short when seq_len is not a multiple of block_size.
+  const int32_t nb = (d->seq_len + d->block_size - 1) / d->block_size;
   const int64_t heads_total = (int64_t)d->batch * d->heads;
-  const int64_t rows = heads_total * (d->seq_len / d->block_size);
+  const int64_t rows = heads_total * nb;
   if (rows >= (int64_t)INT32_MAX)
     return fail(WISE_ERR_UNSUPPORTED, "batch*heads*n_blocks = %lld too large", (long long)rows);
-  *nblk = d->seq_len / d->block_size;
+  *nblk = nb;
   *n_rows = rows;
   return WISE_OK;
 }

@@ -27,9 +27,11 @@
  * - Attention is causal: key j is admissible for query i iff j <= i (the
  *   mask M of Eq. 2).  Scores are (q_i . k_j) * scale, scale = 1/sqrt(head_dim)
  *   unless desc->softmax_scale > 0.
- * - The sequence is cut into blocks of block_size positions (Section 5.1);
- *   n_blocks = seq_len / block_size, and seq_len must be a multiple of
- *   block_size.  A "row" is one (batch, head, query block) triple, numbered
+ * - The sequence is cut into consecutive blocks of block_size positions
+ *   from position 0 (Section 5.1); n_blocks = ceil(seq_len / block_size).
+ *   When seq_len is not a multiple of block_size the last block is short:
+ *   it holds seq_len - (n_blocks - 1) * block_size positions, and that count
+ *   is its |I_q| in Eq. (5).  A "row" is one (batch, head, query block) triple, numbered
  *   r = (b * heads + h) * n_blocks + q; there are batch*heads*n_blocks rows.
  * - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *   stream) and never synchronises the host.  Arguments are validated on the
@@ -51,7 +53,7 @@
 extern "C" {
 #endif
 
-#define WISE_ABI_VERSION 3
+#define WISE_ABI_VERSION 4
 
 typedef enum {
   WISE_OK = 0,
@@ -65,7 +67,7 @@ typedef enum {
 typedef struct {
   int32_t batch;       /* >= 1                                         */
   int32_t heads;       /* >= 1 query heads (Q, O, mass and CSR rows)   */
-  int32_t seq_len;     /* >= block_size, multiple of block_size         */
+  int32_t seq_len;     /* >= 1; the last block may be short            */
   int32_t head_dim;    /* 64, 96 or 128                                 */
   int32_t block_size;  /* B of Section 5.1: 16, 32, 64 or 128 (16: the
                           attention calls need seq_len % 32 == 0; they run
