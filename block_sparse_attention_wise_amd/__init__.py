@@ -171,8 +171,9 @@ def _qkv(q, k, v):
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, torch.bfloat16, 4)
     b, h, s, d = q.shape
+    kvh = k.shape[1]
     if (k.shape != v.shape or k.shape[0] != b or k.shape[2:] != q.shape[2:]
-            or k.shape[1] < 1 or h % k.shape[1] != 0):
+            or not ((kvh >= 1 and h % kvh == 0) or (h == 0 and kvh == 0))):
         raise ValueError(f"q/k/v shapes do not match: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
 
 

@@ -56,13 +56,13 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 // Shape checks common to every call.  Fills nblk / n_rows on success.
 wise_status_t check_desc(const wise_attn_desc_t* d, int32_t* nblk, int64_t* n_rows) {
   if (d == nullptr) return fail(WISE_ERR_INVALID_ARG, "desc is NULL");
-  if (d->batch < 1 || d->heads < 1)
-    return fail(WISE_ERR_INVALID_ARG, "batch (%d) and heads (%d) must be >= 1", d->batch, d->heads);
+  if (d->batch < 0 || d->heads < 0)
+    return fail(WISE_ERR_INVALID_ARG, "batch (%d) and heads (%d) must be >= 0", d->batch, d->heads);
   if (d->block_size != 16 && d->block_size != 32 && d->block_size != 64 && d->block_size != 128)
     return fail(WISE_ERR_UNSUPPORTED, "block_size %d not built (16, 32, 64, 128)", d->block_size);
   if (d->head_dim != 64 && d->head_dim != 96 && d->head_dim != 128)
     return fail(WISE_ERR_UNSUPPORTED, "head_dim %d not built (64, 96, 128)", d->head_dim);
-  if (d->seq_len < 1) return fail(WISE_ERR_INVALID_ARG, "seq_len %d must be >= 1", d->seq_len);
+  if (d->seq_len < 0) return fail(WISE_ERR_INVALID_ARG, "seq_len %d must be >= 0", d->seq_len);
   if (d->seq_len > 65536)
     return fail(WISE_ERR_UNSUPPORTED, "seq_len %d above 65536", d->seq_len);
   if (!std::isfinite(d->softmax_scale))
@@ -98,6 +98,7 @@ wise_status_t run_attn(const wise_attn_desc_t* d, int mode, const void* q, const
   int64_t n_rows;
   wise_status_t st = check_desc(d, &nblk, &n_rows);
   if (st != WISE_OK) return st;
+  if (n_rows == 0) return ok();   // nothing to compute; the pointers are not used
   if ((st = check_tensor(q, "q")) != WISE_OK) return st;
   if ((st = check_tensor(k, "k")) != WISE_OK) return st;
   if ((st = check_tensor(v, "v")) != WISE_OK) return st;
@@ -221,7 +222,7 @@ wise_status_t wise_select_support(const wise_attn_desc_t* desc, const float* mas
   int64_t n_rows;
   wise_status_t st = check_desc(desc, &nblk, &n_rows);
   if (st != WISE_OK) return st;
-  if (mass == nullptr || row_ptr == nullptr || col_idx == nullptr)
+  if (row_ptr == nullptr || (n_rows > 0 && (mass == nullptr || col_idx == nullptr)))
     return fail(WISE_ERR_INVALID_ARG, "mass / row_ptr / col_idx is NULL");
   if ((reinterpret_cast<uintptr_t>(mass) | reinterpret_cast<uintptr_t>(row_ptr) |
        reinterpret_cast<uintptr_t>(col_idx)) & 3u)
@@ -257,7 +258,7 @@ wise_status_t wise_select_variant(const wise_attn_desc_t* desc, int32_t kind, co
   int64_t n_rows;
   wise_status_t st = check_desc(desc, &nblk, &n_rows);
   if (st != WISE_OK) return st;
-  if (step_mass == nullptr || row_ptr == nullptr || col_idx == nullptr)
+  if (row_ptr == nullptr || (n_rows > 0 && (step_mass == nullptr || col_idx == nullptr)))
     return fail(WISE_ERR_INVALID_ARG, "step_mass / row_ptr / col_idx is NULL");
   if ((reinterpret_cast<uintptr_t>(step_mass) | reinterpret_cast<uintptr_t>(row_ptr) |
        reinterpret_cast<uintptr_t>(col_idx)) & 3u)
@@ -298,6 +299,7 @@ wise_status_t wise_support_mass(const wise_attn_desc_t* desc, const float* mass,
   int64_t n_rows;
   wise_status_t st = check_desc(desc, &nblk, &n_rows);
   if (st != WISE_OK) return st;
+  if (n_rows == 0) return ok();
   if (mass == nullptr || row_ptr == nullptr || col_idx == nullptr || retained == nullptr)
     return fail(WISE_ERR_INVALID_ARG, "mass / row_ptr / col_idx / retained is NULL");
   if ((reinterpret_cast<uintptr_t>(mass) | reinterpret_cast<uintptr_t>(row_ptr) |
@@ -317,6 +319,7 @@ wise_status_t wise_support_overlap(const wise_attn_desc_t* desc, const int32_t* 
   int64_t n_rows;
   wise_status_t st = check_desc(desc, &nblk, &n_rows);
   if (st != WISE_OK) return st;
+  if (n_rows == 0) return ok();
   if (row_ptr_a == nullptr || col_idx_a == nullptr || row_ptr_b == nullptr || col_idx_b == nullptr ||
       n_inter == nullptr || n_union == nullptr)
     return fail(WISE_ERR_INVALID_ARG, "a CSR array or an output is NULL");

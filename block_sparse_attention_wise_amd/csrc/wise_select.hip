@@ -277,13 +277,14 @@ __global__ void __launch_bounds__(kScanThreads) scan_rows_kernel(int32_t* row_pt
 template <int EPL>
 hipError_t launch_select_t(const SelectParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)((p.n_rows + kSelWaves - 1) / kSelWaves);
-  hipLaunchKernelGGL(select_count_kernel<EPL>, dim3(grid), dim3(64 * kSelWaves), 0, stream, p);
+  if (grid > 0) hipLaunchKernelGGL(select_count_kernel<EPL>, dim3(grid), dim3(64 * kSelWaves), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(scan_rows_kernel, dim3(1), dim3(kScanThreads), 0, stream, p.row_ptr, p.n_rows);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(select_fill_kernel<EPL>, dim3(grid), dim3(64 * kSelWaves), 0, stream, p);
+  // No rows: the scan alone writes row_ptr[0] = 0.
+  if (grid > 0) hipLaunchKernelGGL(select_fill_kernel<EPL>, dim3(grid), dim3(64 * kSelWaves), 0, stream, p);
   return hipGetLastError();
 }
 

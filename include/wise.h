@@ -33,6 +33,10 @@
  *   it holds seq_len - (n_blocks - 1) * block_size positions, and that count
  *   is its |I_q| in Eq. (5).  A "row" is one (batch, head, query block) triple, numbered
  *   r = (b * heads + h) * n_blocks + q; there are batch*heads*n_blocks rows.
+ * - Empty calls: batch, heads or seq_len may be 0.  A call with
+ *   batch*heads*n_blocks == 0 computes nothing and its tensor pointers may
+ *   be NULL; the selection calls still write row_ptr[0] = 0 (row_ptr must
+ *   then point at that one entry), every other call launches nothing.
  * - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *   stream) and never synchronises the host.  Arguments are validated on the
  *   host first: on any error nothing is launched and nothing is written.
@@ -65,9 +69,9 @@ typedef enum {
 
 /* Shape of one attention call.  All tensors of a call share it. */
 typedef struct {
-  int32_t batch;       /* >= 1                                         */
-  int32_t heads;       /* >= 1 query heads (Q, O, mass and CSR rows)   */
-  int32_t seq_len;     /* >= 1; the last block may be short            */
+  int32_t batch;       /* >= 0                                         */
+  int32_t heads;       /* >= 0 query heads (Q, O, mass and CSR rows)   */
+  int32_t seq_len;     /* >= 0; the last block may be short            */
   int32_t head_dim;    /* 64, 96 or 128                                 */
   int32_t block_size;  /* B of Section 5.1: 16, 32, 64 or 128 (16: the
                           attention calls need seq_len % 32 == 0; they run

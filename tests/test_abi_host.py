@@ -72,6 +72,28 @@ def test_short_last_block_counts(seq, blk, nb):
     assert wise.wise_accum_workspace_bytes(1, 2, seq, 64, blk) == want
 
 
+@pytest.mark.parametrize("b,h,s", [(0, 2, 256), (1, 0, 256), (1, 2, 0)])
+def test_empty_calls_are_no_ops(b, h, s):
+    """batch * heads * n_blocks == 0: every call except the selection ones
+    returns WISE_OK without launching anything, its pointers NULL (so no
+    GPU is needed here); the sizes that depend on the shape are 0."""
+    lib = _lib()
+    for blk in (32, 64, 128):
+        d = _desc(b=b, h=h, s=s, d=128, blk=blk)
+        r = ctypes.byref(d)
+        assert lib.wise_full_attn(r, None, None, None, None, None, None) == wise.WISE_OK
+        assert lib.wise_full_attn_accum(r, None, None, None, None, None, None) == wise.WISE_OK
+        assert lib.wise_full_attn_accum_ws(r, None, None, None, None, None, None, 0, None) == wise.WISE_OK
+        assert lib.wise_sparse_attn(r, None, None, None, None, None, None, None) == wise.WISE_OK
+        assert lib.wise_support_mass(r, None, None, None, None, None) == wise.WISE_OK
+        assert lib.wise_support_overlap(r, None, None, None, None, None, None, None) == wise.WISE_OK
+        assert lib.wise_full_attn_accum_workspace_bytes(r) == 0
+        assert lib.wise_select_max_nnz(r, 0) == 0
+        # the selection calls still need row_ptr (they write its one entry)
+        assert lib.wise_select_support(r, None, 1, 0.9, 0, None, None, 0, None) == wise.WISE_ERR_INVALID_ARG
+        assert lib.wise_select_support(r, None, 0, 0.9, 0, FAKE, None, 0, None) == wise.WISE_ERR_INVALID_ARG
+
+
 def _status(fn, *args):
     return fn(*args)
 
@@ -80,9 +102,9 @@ def test_invalid_descriptors_rejected():
     lib = _lib()
     f = lib.wise_full_attn
     assert f(None, FAKE, FAKE, FAKE, FAKE + 4096, None, None) == wise.WISE_ERR_INVALID_ARG
-    for d, want in [(_desc(b=0), wise.WISE_ERR_INVALID_ARG), (_desc(h=-1), wise.WISE_ERR_INVALID_ARG),
+    for d, want in [(_desc(b=-1), wise.WISE_ERR_INVALID_ARG), (_desc(h=-1), wise.WISE_ERR_INVALID_ARG),
                     (_desc(d=80), wise.WISE_ERR_UNSUPPORTED), (_desc(blk=48), wise.WISE_ERR_UNSUPPORTED),
-                    (_desc(s=0), wise.WISE_ERR_INVALID_ARG), (_desc(s=-32), wise.WISE_ERR_INVALID_ARG),
+                    (_desc(s=-1), wise.WISE_ERR_INVALID_ARG), (_desc(s=-32), wise.WISE_ERR_INVALID_ARG),
                     (_desc(s=131072), wise.WISE_ERR_UNSUPPORTED),
                     (_desc(scale=float("nan")), wise.WISE_ERR_INVALID_ARG)]:
         # bad desc, null o: the desc check must fire first or the pointer check; either way no launch

@@ -96,3 +96,30 @@ def test_sparse_malformed_row_pointers_read_in_bounds():
         compare_outputs(got[0, hh], ref, f"h{hh}")
     # the empty row gives zeros
     assert np.all(got[0, 0, blk:2 * blk] == 0.0)
+
+
+@pytest.mark.parametrize("shape", [(0, 2, 256, 64), (1, 0, 256, 64), (1, 2, 0, 64)],
+                         ids=["batch0", "heads0", "seq0"])
+def test_empty_inputs_are_no_ops(shape):
+    """Zero batch, heads or sequence length: every call succeeds and computes
+    nothing; the selection calls write the CSR of zero rows, row_ptr = [0]."""
+    b, h, s, d = shape
+    blk = 64
+    nb = -(-s // blk)
+    say(f"empty inputs {shape}")
+    q, k, v = (torch.empty(shape, dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    assert wise.wise_full_attn(q, k, v, blk).shape == shape
+    mass = torch.zeros(b, h, nb, nb, dtype=torch.float32, device="cuda")
+    wise.wise_full_attn_accum(q, k, v, mass, blk)
+    wise.wise_full_attn_accum_ws(q, k, v, mass, blk)
+    rp = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    rp, ci = wise.wise_select_support(mass, 1, 0.9, d, blk, row_ptr=rp)
+    rp_u = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    rp_u, ci_u = wise.wise_select_variant(wise.SELECT_UNION, torch.stack([mass, mass]).contiguous(), 0.9, d, blk,
+                                          row_ptr=rp_u)
+    o = wise.wise_sparse_attn(q, k, v, rp, ci, blk)
+    ret = wise.wise_support_mass(mass, rp, ci, d, blk)
+    inter, uni = wise.wise_support_overlap((rp, ci), (rp_u, ci_u), b, h, nb, d, blk)
+    torch.cuda.synchronize()
+    assert rp.cpu().tolist() == [0] and rp_u.cpu().tolist() == [0]
+    assert o.shape == shape and ret.numel() == 0 and inter.numel() == 0 and uni.numel() == 0
