@@ -10,7 +10,9 @@ the sparse launch on messy CSR rows (empty,
 the full causal row, random entries with repeats, entries outside [0, q]
 that the kernel must ignore, unsorted), and checks each against the fp64
 oracle: O to the output tolerance, the LSE to bf16-operand accuracy, the
-block mass to fp32 accuracy.
+block mass to fp32 accuracy.  Cases from N_CASES on also cut the sequence
+short of a whole last block (block sizes 32-128; block 16 attention needs
+whole 32-key tiles), so that block holds between 1 and B - 1 positions.
 """
 import numpy as np
 import pytest
@@ -25,6 +27,7 @@ pytestmark = pytest.mark.gpu
 wise = pytest.importorskip("block_sparse_attention_wise_amd")
 
 N_CASES = 48
+N_SHORT = 16
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -46,7 +49,13 @@ def _case(seed):
     grp = int(rng.choice([1, 2, 4]))
     scale = 0.0 if rng.random() < 0.5 else float(rng.uniform(0.02, 0.3))   # 0: 1/sqrt(d)
     amp = float(rng.choice([1.0, 4.0]))
-    return rng, dict(d=d, blk=blk, nb=nb, s=nb * blk, b=b, kvh=kvh, h=kvh * grp, grp=grp,
+    s = nb * blk
+    if seed >= N_CASES:
+        if blk == 16:
+            blk = 32
+            s = nb * blk
+        s -= int(rng.integers(1, blk))            # a short last block of 1..B-1 positions
+    return rng, dict(d=d, blk=blk, nb=nb, s=s, b=b, kvh=kvh, h=kvh * grp, grp=grp,
                      scale=scale, amp=amp)
 
 
@@ -67,7 +76,7 @@ def _messy_rows(rng, n_rows, nb):
     return rows
 
 
-@pytest.mark.parametrize("seed", range(N_CASES))
+@pytest.mark.parametrize("seed", range(N_CASES + N_SHORT))
 def test_random_case(seed):
     rng, c = _case(seed)
     say(f"random case {seed}: {c}")
