@@ -98,8 +98,9 @@ wise_status_t wise_full_attn(const wise_attn_desc_t* desc, const void* q, const 
 
 /*
  * Discovery step: dense causal attention (Eq. 2) plus the block mass of
- * Section 5.1, Eq. (5), r_qb = (1/B) sum_{i in I_q} sum_{j in I_b, j<=i} A_ij,
- * added in place:  mass[b][h][q][kb] += r_qb  for kb <= q.
+ * Section 5.1, Eq. (5), r_qb = (1/|I_q|) sum_{i in I_q} sum_{j in I_b, j<=i} A_ij
+ * (|I_q| = block_size, or the short last block's length), added in place:
+ * mass[b][h][q][kb] += r_qb  for kb <= q.
  *
  * q, k, v, o: as in wise_full_attn.
  * mass: fp32 [batch][heads][n_blocks][n_blocks], read-modify-written.  The
