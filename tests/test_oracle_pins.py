@@ -530,10 +530,13 @@ def test_trajectory_eta_one_late_equals_dense(S):
     np.testing.assert_allclose(row_sums, 2.0, rtol=0, atol=1e-13)
 
 
-def test_trajectory_supports_keep_sink_and_diagonal():
-    S, D, B = 128, 8, 16
+@pytest.mark.parametrize("S", [128, 123])
+def test_trajectory_supports_keep_sink_and_diagonal(S):
+    D, B = 8, 16
     steps = [_rand(50 + t, S, D) for t in range(4)]
     out = oracle.trajectory_head(steps, td=2, block=B, eta=0.5, cap=1)
+    assert sorted(out["supports"]) == list(range(8))
+    np.testing.assert_allclose(out["mass_sum"].sum(axis=1), 2.0, rtol=0, atol=1e-13)
     for qb, sup in out["supports"].items():
         assert 0 in sup and qb in sup and sup == sorted(sup)
         assert len(sup) <= 3
