@@ -8,10 +8,13 @@ perturbation property of Appendix A.1, and hand-derived golden fixtures.
 The mutation tests at the end plant typical mistakes into copies of the
 oracle's functions and require at least one pin to fail for each.
 """
+import contextlib
+import inspect
 import itertools
 import json
 import math
 import os
+import textwrap
 from fractions import Fraction
 from types import SimpleNamespace
 
@@ -36,7 +39,12 @@ def _impl(**over):
                          select_size_matched=oracle.select_size_matched,
                          retained_mass=oracle.retained_mass,
                          rolling_working_set=oracle.rolling_working_set,
-                         jaccard=oracle.jaccard)
+                         jaccard=oracle.jaccard,
+                         default_scale=oracle.default_scale,
+                         dense_attention=oracle.dense_attention,
+                         mean_block_mass=oracle.mean_block_mass,
+                         support_margins=oracle.support_margins,
+                         trajectory_head=oracle.trajectory_head)
     for k, v in over.items():
         setattr(ns, k, v)
     return ns
@@ -472,6 +480,75 @@ def pin_short_last_block_prefix(impl):
                          - a_s)) <= 1e-15
 
 
+def pin_default_scale(impl):
+    """Eq. (2): the softmax temperature is 1/sqrt(d_h).  Exact values at
+    d_h = 4, 16, 64, 256, and through dense attention with no scale given:
+    two keys whose dot products with q differ by 4x at d_h = 4 give
+    A_11 = logistic(4x / 2)."""
+    for d, want in ((4, 0.5), (16, 0.25), (64, 0.125), (256, 0.0625)):
+        assert impl.default_scale(d) == want, (d, impl.default_scale(d))
+    x = 0.3
+    q = np.ones((2, 4))
+    k = np.vstack([np.zeros(4), np.full(4, x)])
+    v = np.array([[0.0] * 4, [1.0] * 4])
+    o = impl.dense_attention(q, k, v)
+    assert abs(o[1, 0] - expit(4 * x / 2)) < 1e-15, o[1, 0]
+
+
+def pin_mean_block_mass_closed_form(impl):
+    """The discovery steps' masses combine as their equal-weight mean
+    (dyadic rows, exact), and the mean of rows that each sum to one sums to
+    one."""
+    rows = [np.array([1.0, 0.0, 0.0]), np.array([0.5, 0.5, 0.0]), np.array([0.0, 0.25, 0.75])]
+    got = impl.mean_block_mass(rows)
+    assert np.array_equal(got, np.array([0.5, 0.25, 0.25])), got
+    g = np.random.default_rng(35)
+    steps = [g.dirichlet(np.ones(9), size=4) for _ in range(5)]
+    np.testing.assert_allclose(impl.mean_block_mass(steps).sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    one = impl.mean_block_mass([steps[2]])
+    np.testing.assert_allclose(one, steps[2], rtol=0, atol=0)
+
+
+def _golden_discovery():
+    with open(os.path.join(GOLDEN, "discovery_mean_dyadic.json")) as f:
+        g = json.load(f)
+    S = g["seq_len"]
+    qkv = []
+    for w in g["weights_x64"]:
+        q = np.ones((S, 1))
+        k = np.log(np.array(w, dtype=np.float64) / 64.0)[:, None]
+        v = np.array(g["values"], dtype=np.float64)[:, None]
+        qkv.append((q, k, v))
+    return g, qkv
+
+
+def pin_trajectory_selects_on_mean(impl):
+    """Section 5.1-5.2 on a hand-worked trajectory: the support is chosen on
+    the mean of the discovery masses (not on the last or first step, their
+    union or their sum), and the late step attends inside it."""
+    g, qkv = _golden_discovery()
+    qb = g["query_block"]
+    out = impl.trajectory_head(qkv, g["td"], g["block"], g["eta"], qblocks=[qb], scale=1.0)
+    assert out["supports"][qb] == g["support"], out["supports"][qb]
+    np.testing.assert_allclose(out["mass_sum"][0], np.array(g["mass_sum_x64"]) / 64.0, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(out["mass_mean"][0], np.array(g["mass_mean_x128"]) / 128.0, rtol=0, atol=1e-15)
+    late = out["outputs"][g["td"]]
+    assert abs(late[0, 0] - _frac(g["late_output"])) < 1e-14, late
+
+
+def pin_margins_golden(impl):
+    """Appendix A.1, Eq. (13), hand-derived on dyadic rows with k* = 3, one
+    where delta_minus / (k* - 1) is the binding term and one where
+    delta_plus / k* is."""
+    with open(os.path.join(GOLDEN, "margins_dyadic.json")) as f:
+        g = json.load(f)
+    for case in g["cases"]:
+        m = impl.support_margins(np.array(case["mbar_x32"]) / 32.0, case["q"], case["eta_x64"] / 64.0)
+        assert m["k_star"] == case["k_star"], (case["note"], m)
+        for key in ("delta_rank", "delta_minus", "delta_plus", "Delta"):
+            assert abs(m[key] - _frac(case[key])) < 1e-16, (case["note"], key, m[key])
+
+
 PINS = [pin_uniform_when_q_zero, pin_constant_values, pin_single_position,
         pin_logistic_two_keys, pin_causal_rows_sum_to_one, pin_key_shift_invariance,
         pin_scale_is_a_temperature, pin_golden_dense, pin_block_mass_sums_to_one,
@@ -483,7 +560,8 @@ PINS = [pin_uniform_when_q_zero, pin_constant_values, pin_single_position,
         pin_sink_and_diagonal_support, pin_masked_rows_normalised,
         pin_variants_golden, pin_eta_support_brute_force, pin_union_structure,
         pin_matched_controls, pin_retained_mass, pin_rolling_and_jaccard,
-        pin_short_last_block_mass, pin_short_last_block_prefix]
+        pin_short_last_block_mass, pin_short_last_block_prefix, pin_default_scale,
+        pin_mean_block_mass_closed_form, pin_trajectory_selects_on_mean, pin_margins_golden]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -558,7 +636,7 @@ def _caught(impl):
     for pin in PINS:
         try:
             pin(impl)
-        except AssertionError:
+        except Exception:        # a failed assertion, or a planted mistake that crashes
             return True
     return False
 
@@ -727,3 +805,69 @@ MUTANTS = {
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_planted_mistake(name):
     assert _caught(_impl(**MUTANTS[name])), name
+
+
+# Mistakes planted into the oracle's own source: a copy of the function with
+# one edit, compiled against the oracle module's namespace and swapped into
+# the module while every pin runs, so that the oracle's internal calls (the
+# trajectory calling the mean, dense attention calling the default scale)
+# reach the mutant too.
+
+def _source_mutant(func, old, new):
+    src = textwrap.dedent(inspect.getsource(func))
+    assert src.count(old) == 1, (func.__name__, old)
+    local = {}
+    exec(compile(src.replace(old, new), f"<mutant of {func.__name__}>", "exec"), vars(oracle), local)
+    return local[func.__name__]
+
+
+@contextlib.contextmanager
+def _swapped(name, fn):
+    saved = getattr(oracle, name)
+    setattr(oracle, name, fn)
+    try:
+        yield
+    finally:
+        setattr(oracle, name, saved)
+
+
+SOURCE_MUTANTS = {
+    "mean_divides_by_steps_plus_one": (oracle.mean_block_mass, "acc / len(step_masses)",
+                                       "acc / (len(step_masses) + 1)"),
+    "trajectory_selects_on_last_step": (oracle.trajectory_head, "mbar = mean_block_mass(masses)",
+                                        "mbar = masses[-1]"),
+    "trajectory_selects_on_first_step": (oracle.trajectory_head, "mbar = mean_block_mass(masses)",
+                                         "mbar = masses[0]"),
+    "trajectory_selects_on_sum": (oracle.trajectory_head, "mbar = mean_block_mass(masses)",
+                                  "mbar = sum(masses)"),
+    "trajectory_late_step_dense": (oracle.trajectory_head,
+                                   "outputs.append(masked_attention(q, k, v, supports, block, sc, rows)",
+                                   "outputs.append(dense_attention(q, k, v, sc, rows)"),
+    "default_scale_one_over_d": (oracle.default_scale, "1.0 / math.sqrt(head_dim)", "1.0 / head_dim"),
+    "margins_minus_over_k": (oracle.support_margins, "d_minus / (k_star - 1)", "d_minus / k_star"),
+    "margins_plus_over_k_minus_1": (oracle.support_margins, "d_plus / k_star)", "d_plus / max(1, k_star - 1))"),
+    "margins_rank_not_halved": (oracle.support_margins, "(vals[k_star - 1] - vals[k_star]) / 2",
+                                "(vals[k_star - 1] - vals[k_star])"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SOURCE_MUTANTS))
+def test_pins_catch_mistake_in_oracle_source(name):
+    func, old, new = SOURCE_MUTANTS[name]
+    mutant = _source_mutant(func, old, new)
+    with _swapped(func.__name__, mutant):
+        assert _caught(_impl()), name
+    assert getattr(oracle, func.__name__) is func
+
+
+def test_unmutated_source_copy_passes_every_pin():
+    """The mutant harness itself: an unedited copy of each function, swapped
+    in the same way, passes every pin."""
+    for func in {m[0] for m in SOURCE_MUTANTS.values()}:
+        src = textwrap.dedent(inspect.getsource(func))
+        first = src.splitlines()[0]
+        copy = _source_mutant(func, first, first)
+        with _swapped(func.__name__, copy):
+            impl = _impl()
+            for pin in PINS:
+                pin(impl)
