@@ -17,6 +17,7 @@ Layouts (see the header for the full contract):
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional, Tuple
@@ -27,13 +28,14 @@ __all__ = ["WiseError", "WiseDesc", "load_library", "library_path", "wise_full_a
            "SELECT_UNION", "SELECT_STATIC", "SELECT_MASS_MATCHED", "SELECT_SIZE_MATCHED",
            "wise_support_mass", "wise_support_overlap",
            "wise_select_max_nnz", "wise_abi_version", "WISE_OK", "WISE_ERR_INVALID_ARG",
-           "WISE_ERR_UNSUPPORTED", "WISE_ERR_CAPACITY", "WISE_ERR_HIP"]
+           "WISE_ERR_UNSUPPORTED", "WISE_ERR_CAPACITY", "WISE_ERR_HIP", "WISE_ERR_OVERFLOW"]
 
 WISE_OK = 0
 WISE_ERR_INVALID_ARG = 1
 WISE_ERR_UNSUPPORTED = 2
 WISE_ERR_CAPACITY = 3
 WISE_ERR_HIP = 4
+WISE_ERR_OVERFLOW = 5   # reserved by the ABI, never returned
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -75,8 +77,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "wise_full_attn_accum": ([dp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "wise_full_attn_accum_ws": ([dp, vp, vp, vp, vp, vp, vp, i64, vp], ctypes.c_int),
         "wise_full_attn_accum_workspace_bytes": ([dp], i64),
-        "wise_select_support": ([dp, vp, i32, ctypes.c_double, i32, vp, vp, i64, vp], ctypes.c_int),
-        "wise_select_variant": ([dp, i32, vp, i32, ctypes.c_double, vp, vp, i64, vp], ctypes.c_int),
+        "wise_select_support": ([dp, vp, i32, ctypes.c_double, i32, vp, vp, i64, vp, vp], ctypes.c_int),
+        "wise_select_variant": ([dp, i32, vp, i32, ctypes.c_double, vp, vp, i64, vp, vp], ctypes.c_int),
         "wise_support_mass": ([dp, vp, vp, vp, vp, vp], ctypes.c_int),
         "wise_support_overlap": ([dp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "wise_sparse_attn": ([dp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
@@ -96,7 +98,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
 
 def _status_name(status: int) -> str:
     return {0: "WISE_OK", 1: "WISE_ERR_INVALID_ARG", 2: "WISE_ERR_UNSUPPORTED",
-            3: "WISE_ERR_CAPACITY", 4: "WISE_ERR_HIP"}.get(status, "?")
+            3: "WISE_ERR_CAPACITY", 4: "WISE_ERR_HIP", 5: "WISE_ERR_OVERFLOW"}.get(status, "?")
 
 
 def _check(status: int, func: str) -> None:
@@ -126,6 +128,16 @@ def _stream_ptr(stream) -> Optional[int]:
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
+
+
+def _alloc_on(stream):
+    """Context for the tensors this binding allocates (outputs, workspace):
+    with a caller's ``stream`` they are allocated on that stream, so torch's
+    caching allocator does not hand their memory to other work before the
+    kernels that use them on that stream have run."""
+    if stream is None:
+        return contextlib.nullcontext()
+    return _torch().cuda.stream(stream)
 
 
 def _need(t, name, dtype, ndim=None):
@@ -177,10 +189,11 @@ def _qkv(q, k, v):
         raise ValueError(f"q/k/v shapes do not match: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
 
 
-def _out(o, q):
+def _out(o, q, stream=None):
     torch = _torch()
     if o is None:
-        return torch.empty_like(q)
+        with _alloc_on(stream):
+            return torch.empty_like(q)
     _need(o, "o", torch.bfloat16, 4)
     if o.shape != q.shape:
         raise ValueError("o must have q's shape")
@@ -193,7 +206,7 @@ def wise_full_attn(q, k, v, block_size: int, o=None, lse=None, softmax_scale: fl
     torch = _torch()
     block_size = _block(block_size)
     _qkv(q, k, v)
-    o = _out(o, q)
+    o = _out(o, q, stream)
     lse_ptr = None
     named = [(q, "q"), (k, "k"), (v, "v"), (o, "o")]
     if lse is not None:
@@ -224,7 +237,7 @@ def wise_full_attn_accum(q, k, v, mass, block_size: int, o=None, softmax_scale: 
     _need(mass, "mass", torch.float32, 4)
     if tuple(mass.shape) != _mass_shape(q, block_size):
         raise ValueError(f"mass must be {_mass_shape(q, block_size)}, got {tuple(mass.shape)}")
-    o = _out(o, q)
+    o = _out(o, q, stream)
     dev = _same_device((q, "q"), (k, "k"), (v, "v"), (o, "o"), (mass, "mass"))
     d = _desc(q, block_size, softmax_scale, k)
     _call("wise_full_attn_accum", dev, stream, ctypes.byref(d), q.data_ptr(), k.data_ptr(),
@@ -253,11 +266,12 @@ def wise_full_attn_accum_ws(q, k, v, mass, block_size: int, o=None, workspace=No
     _need(mass, "mass", torch.float32, 4)
     if tuple(mass.shape) != _mass_shape(q, block_size):
         raise ValueError(f"mass must be {_mass_shape(q, block_size)}, got {tuple(mass.shape)}")
-    o = _out(o, q)
+    o = _out(o, q, stream)
     b, h, s, dh = q.shape
     need = wise_accum_workspace_bytes(b, h, s, dh, block_size)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        with _alloc_on(stream):     # freed on return: its block must stay with `stream`
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     named = [(q, "q"), (k, "k"), (v, "v"), (o, "o"), (mass, "mass")]
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
@@ -280,13 +294,24 @@ def wise_select_max_nnz(batch: int, heads: int, seq_len: int, head_dim: int, blo
     return int(n)
 
 
+def _nnz_ptr(nnz, dev):
+    if nnz is None:
+        return None
+    torch = _torch()
+    _need(nnz, "nnz", torch.int64, 1)
+    if nnz.numel() != 1 or nnz.device != dev:
+        raise ValueError("nnz must be one int64 on the mass tensor's GPU")
+    return nnz.data_ptr()
+
+
 def wise_select_support(mass, n_steps: int, eta: float, head_dim: int, block_size: int,
-                        max_blocks: int = 0, row_ptr=None, col_idx=None,
+                        max_blocks: int = 0, row_ptr=None, col_idx=None, nnz=None,
                         stream=None) -> Tuple[object, object]:
     """Working-set selection (Eq. 6 + sink/diagonal) -> (row_ptr, col_idx) CSR.
 
     ``col_idx`` is sized to the worst case; its first ``row_ptr[-1]`` entries
-    are meaningful.
+    are meaningful.  ``nnz`` (optional, int64 [1] on the GPU) receives that
+    count on the device.
     """
     torch = _torch()
     block_size = _block(block_size)
@@ -298,17 +323,19 @@ def wise_select_support(mass, n_steps: int, eta: float, head_dim: int, block_siz
     d = WiseDesc(b, h, seq, head_dim, block_size, 0.0)
     cap = wise_select_max_nnz(b, h, seq, head_dim, block_size, max_blocks)
     n_rows = b * h * nb
-    if row_ptr is None:
-        row_ptr = torch.empty(n_rows + 1, dtype=torch.int32, device=mass.device)
-    if col_idx is None:
-        col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=mass.device)
+    with _alloc_on(stream):
+        if row_ptr is None:
+            row_ptr = torch.empty(n_rows + 1, dtype=torch.int32, device=mass.device)
+        if col_idx is None:
+            col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=mass.device)
     _need(row_ptr, "row_ptr", torch.int32, 1)
     _need(col_idx, "col_idx", torch.int32, 1)
     if row_ptr.numel() != n_rows + 1:
         raise ValueError(f"row_ptr must have {n_rows + 1} entries")
     dev = _same_device((mass, "mass"), (row_ptr, "row_ptr"), (col_idx, "col_idx"))
     _call("wise_select_support", dev, stream, ctypes.byref(d), mass.data_ptr(), int(n_steps),
-          float(eta), int(max_blocks), row_ptr.data_ptr(), col_idx.data_ptr(), col_idx.numel())
+          float(eta), int(max_blocks), row_ptr.data_ptr(), col_idx.data_ptr(), col_idx.numel(),
+          _nnz_ptr(nnz, dev))
     return row_ptr, col_idx
 
 
@@ -316,7 +343,7 @@ SELECT_UNION, SELECT_STATIC, SELECT_MASS_MATCHED, SELECT_SIZE_MATCHED = 1, 2, 3,
 
 
 def wise_select_variant(kind: int, step_mass, eta: float, head_dim: int, block_size: int,
-                        row_ptr=None, col_idx=None, stream=None) -> Tuple[object, object]:
+                        row_ptr=None, col_idx=None, nnz=None, stream=None) -> Tuple[object, object]:
     """Selection variants (temporal union, Static, MassMatched, SizeMatched)
     over single-step masses ``step_mass`` [n_mass, batch, heads, nB, nB]
     -> (row_ptr, col_idx) CSR."""
@@ -330,17 +357,18 @@ def wise_select_variant(kind: int, step_mass, eta: float, head_dim: int, block_s
     d = WiseDesc(b, h, seq, head_dim, block_size, 0.0)
     cap = wise_select_max_nnz(b, h, seq, head_dim, block_size, 0)
     n_rows = b * h * nb
-    if row_ptr is None:
-        row_ptr = torch.empty(n_rows + 1, dtype=torch.int32, device=step_mass.device)
-    if col_idx is None:
-        col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=step_mass.device)
+    with _alloc_on(stream):
+        if row_ptr is None:
+            row_ptr = torch.empty(n_rows + 1, dtype=torch.int32, device=step_mass.device)
+        if col_idx is None:
+            col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=step_mass.device)
     _need(row_ptr, "row_ptr", torch.int32, 1)
     _need(col_idx, "col_idx", torch.int32, 1)
     if row_ptr.numel() != n_rows + 1:
         raise ValueError(f"row_ptr must have {n_rows + 1} entries")
     dev = _same_device((step_mass, "step_mass"), (row_ptr, "row_ptr"), (col_idx, "col_idx"))
     _call("wise_select_variant", dev, stream, ctypes.byref(d), int(kind), step_mass.data_ptr(), int(n_mass),
-          float(eta), row_ptr.data_ptr(), col_idx.data_ptr(), col_idx.numel())
+          float(eta), row_ptr.data_ptr(), col_idx.data_ptr(), col_idx.numel(), _nnz_ptr(nnz, dev))
     return row_ptr, col_idx
 
 
@@ -357,7 +385,8 @@ def wise_support_mass(mass, row_ptr, col_idx, head_dim: int, block_size: int, re
     if row_ptr.numel() != n_rows + 1:
         raise ValueError(f"row_ptr must have {n_rows + 1} entries")
     if retained is None:
-        retained = torch.empty(n_rows, dtype=torch.float32, device=mass.device)
+        with _alloc_on(stream):
+            retained = torch.empty(n_rows, dtype=torch.float32, device=mass.device)
     _need(retained, "retained", torch.float32, 1)
     if retained.numel() != n_rows:
         raise ValueError(f"retained must have {n_rows} entries")
@@ -380,8 +409,9 @@ def wise_support_overlap(csr_a, csr_b, batch: int, heads: int, n_blocks: int, he
     if ra.numel() != n_rows + 1 or rb.numel() != n_rows + 1:
         raise ValueError(f"row_ptr arrays must have {n_rows + 1} entries")
     dev = _same_device((ra, "row_ptr_a"), (ca, "col_idx_a"), (rb, "row_ptr_b"), (cb, "col_idx_b"))
-    inter = torch.empty(n_rows, dtype=torch.int32, device=dev)
-    uni = torch.empty(n_rows, dtype=torch.int32, device=dev)
+    with _alloc_on(stream):
+        inter = torch.empty(n_rows, dtype=torch.int32, device=dev)
+        uni = torch.empty(n_rows, dtype=torch.int32, device=dev)
     d = WiseDesc(batch, heads, n_blocks * block_size, head_dim, block_size, 0.0)
     _call("wise_support_overlap", dev, stream, ctypes.byref(d), ra.data_ptr(), ca.data_ptr(), rb.data_ptr(),
           cb.data_ptr(), inter.data_ptr(), uni.data_ptr())
@@ -399,7 +429,7 @@ def wise_sparse_attn(q, k, v, row_ptr, col_idx, block_size: int, o=None,
     b, h, s, _ = q.shape
     if row_ptr.numel() != b * h * -(-s // block_size) + 1:
         raise ValueError("row_ptr must have batch*heads*n_blocks + 1 entries")
-    o = _out(o, q)
+    o = _out(o, q, stream)
     dev = _same_device((q, "q"), (k, "k"), (v, "v"), (o, "o"), (row_ptr, "row_ptr"), (col_idx, "col_idx"))
     d = _desc(q, block_size, softmax_scale, k)
     _call("wise_sparse_attn", dev, stream, ctypes.byref(d), q.data_ptr(), k.data_ptr(),

@@ -217,7 +217,7 @@ int64_t wise_select_max_nnz(const wise_attn_desc_t* desc, int32_t max_blocks) {
 
 wise_status_t wise_select_support(const wise_attn_desc_t* desc, const float* mass, int32_t n_steps,
                                   double eta, int32_t max_blocks, int32_t* row_ptr, int32_t* col_idx,
-                                  int64_t col_capacity, void* stream) {
+                                  int64_t col_capacity, int64_t* nnz, void* stream) {
   int32_t nblk;
   int64_t n_rows;
   wise_status_t st = check_desc(desc, &nblk, &n_rows);
@@ -227,6 +227,7 @@ wise_status_t wise_select_support(const wise_attn_desc_t* desc, const float* mas
   if ((reinterpret_cast<uintptr_t>(mass) | reinterpret_cast<uintptr_t>(row_ptr) |
        reinterpret_cast<uintptr_t>(col_idx)) & 3u)
     return fail(WISE_ERR_INVALID_ARG, "mass / row_ptr / col_idx not 4-byte aligned");
+  if (reinterpret_cast<uintptr_t>(nnz) & 7u) return fail(WISE_ERR_INVALID_ARG, "nnz not 8-byte aligned");
   if (n_steps < 1) return fail(WISE_ERR_INVALID_ARG, "n_steps %d must be >= 1", n_steps);
   if (!(eta > 0.0 && eta <= 1.0)) return fail(WISE_ERR_INVALID_ARG, "eta %g outside (0, 1]", eta);
   if (max_blocks < 0) return fail(WISE_ERR_INVALID_ARG, "max_blocks %d < 0", max_blocks);
@@ -246,6 +247,7 @@ wise_status_t wise_select_support(const wise_attn_desc_t* desc, const float* mas
   p.max_blocks = max_blocks;
   p.n_steps = (double)n_steps;
   p.eta = eta;
+  p.nnz = nnz;
   const hipError_t e = launch_select(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(WISE_ERR_HIP, "selection launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -253,7 +255,7 @@ wise_status_t wise_select_support(const wise_attn_desc_t* desc, const float* mas
 
 wise_status_t wise_select_variant(const wise_attn_desc_t* desc, int32_t kind, const float* step_mass,
                                   int32_t n_mass, double eta, int32_t* row_ptr, int32_t* col_idx,
-                                  int64_t col_capacity, void* stream) {
+                                  int64_t col_capacity, int64_t* nnz, void* stream) {
   int32_t nblk;
   int64_t n_rows;
   wise_status_t st = check_desc(desc, &nblk, &n_rows);
@@ -263,6 +265,7 @@ wise_status_t wise_select_variant(const wise_attn_desc_t* desc, int32_t kind, co
   if ((reinterpret_cast<uintptr_t>(step_mass) | reinterpret_cast<uintptr_t>(row_ptr) |
        reinterpret_cast<uintptr_t>(col_idx)) & 3u)
     return fail(WISE_ERR_INVALID_ARG, "step_mass / row_ptr / col_idx not 4-byte aligned");
+  if (reinterpret_cast<uintptr_t>(nnz) & 7u) return fail(WISE_ERR_INVALID_ARG, "nnz not 8-byte aligned");
   if (kind < WISE_SELECT_UNION || kind > WISE_SELECT_SIZE_MATCHED)
     return fail(WISE_ERR_INVALID_ARG, "unknown selection kind %d", kind);
   const int32_t min_mass = (kind == WISE_SELECT_UNION || kind == WISE_SELECT_STATIC) ? 1 : 2;
@@ -288,6 +291,7 @@ wise_status_t wise_select_variant(const wise_attn_desc_t* desc, int32_t kind, co
   p.kind = kind;
   p.n_mass = n_mass;
   p.mass_stride = n_rows * nblk;
+  p.nnz = nnz;
   const hipError_t e = launch_select(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(WISE_ERR_HIP, "selection launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -341,6 +345,7 @@ const char* wise_status_string(wise_status_t status) {
     case WISE_ERR_UNSUPPORTED: return "WISE_ERR_UNSUPPORTED";
     case WISE_ERR_CAPACITY: return "WISE_ERR_CAPACITY";
     case WISE_ERR_HIP: return "WISE_ERR_HIP";
+    case WISE_ERR_OVERFLOW: return "WISE_ERR_OVERFLOW";
   }
   return "WISE_ERR_UNKNOWN";
 }

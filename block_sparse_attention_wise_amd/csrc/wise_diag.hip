@@ -27,7 +27,8 @@ constexpr int kMaxWords = 32;   // 64 * 32 = 2048 blocks per row
 __device__ __forceinline__ uint32_t row_bits(const int32_t* row_ptr, const int32_t* col_idx, int row, int q,
                                              int lane) {
   int e0 = row_ptr[row], e1 = row_ptr[row + 1];
-  if (e1 < e0) e1 = e0;
+  if (e0 < 0) e0 = 0;          // malformed pointers: read nothing before col_idx
+  if (e1 < e0) e1 = e0;        // and a decreasing pair as an empty row
   uint32_t bits = 0;
   for (int base = e0; base < e1; base += 64) {
     const int idx = base + lane;

@@ -75,6 +75,7 @@ struct SelectParams {
   int32_t kind;        // SelectKind
   int32_t n_mass;      // step masses given (variants)
   int64_t mass_stride; // elements between consecutive step masses
+  int64_t* nnz;        // optional: total entries, written after the scan
 };
 
 hipError_t launch_select(const SelectParams& p, hipStream_t stream);

@@ -231,11 +231,12 @@ __global__ void __launch_bounds__(64 * kSelWaves) select_fill_kernel(SelectParam
 }
 
 // In-place inclusive scan of row_ptr[1..n] (row lengths) with row_ptr[0] = 0,
-// by one workgroup of 1024 threads walking the rows in chunks.
+// by one workgroup of 1024 threads walking the rows in chunks; the total
+// goes to *nnz as well when nnz is given.
 constexpr int kScanThreads = 1024;
 constexpr int kScanItems = 8;
 
-__global__ void __launch_bounds__(kScanThreads) scan_rows_kernel(int32_t* row_ptr, int n) {
+__global__ void __launch_bounds__(kScanThreads) scan_rows_kernel(int32_t* row_ptr, int n, int64_t* nnz) {
   __shared__ int wsum[kScanThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int carry = 0;
@@ -272,6 +273,7 @@ __global__ void __launch_bounds__(kScanThreads) scan_rows_kernel(int32_t* row_pt
     }
     carry += total;
   }
+  if (nnz != nullptr && tid == 0) *nnz = carry;
 }
 
 template <int EPL>
@@ -280,7 +282,7 @@ hipError_t launch_select_t(const SelectParams& p, hipStream_t stream) {
   if (grid > 0) hipLaunchKernelGGL(select_count_kernel<EPL>, dim3(grid), dim3(64 * kSelWaves), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(scan_rows_kernel, dim3(1), dim3(kScanThreads), 0, stream, p.row_ptr, p.n_rows);
+  hipLaunchKernelGGL(scan_rows_kernel, dim3(1), dim3(kScanThreads), 0, stream, p.row_ptr, p.n_rows, p.nnz);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // No rows: the scan alone writes row_ptr[0] = 0.

@@ -24,9 +24,10 @@
  *   [batch][heads][seq_len][head_dim] (K and V: [batch][kv_heads][...]).
  *   Q, K and V are read-only; O may not alias them.  All pointers must be
  *   16-byte aligned.
- * - Attention is causal: key j is admissible for query i iff j <= i (the
- *   mask M of Eq. 2).  Scores are (q_i . k_j) * scale, scale = 1/sqrt(head_dim)
- *   unless desc->softmax_scale > 0.
+ * - Attention is always causal: key j is admissible for query i iff j <= i
+ *   (the mask M of Eq. 2); the descriptor has no switch for it.  Scores are
+ *   (q_i . k_j) * scale, scale = 1/sqrt(head_dim) unless
+ *   desc->softmax_scale > 0.
  * - The sequence is cut into consecutive blocks of block_size positions
  *   from position 0 (Section 5.1); n_blocks = ceil(seq_len / block_size).
  *   When seq_len is not a multiple of block_size the last block is short:
@@ -37,8 +38,9 @@
  *   batch*heads*n_blocks == 0 computes nothing and its tensor pointers may
  *   be NULL; the selection calls still write row_ptr[0] = 0 (row_ptr must
  *   then point at that one entry), every other call launches nothing.
- * - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
- *   stream) and never synchronises the host.  Arguments are validated on the
+ * - Every call is asynchronous on `stream` (a hipStream_t passed as void*,
+ *   so that this header needs no HIP include; NULL = the null stream) and
+ *   never synchronises the host.  Arguments are validated on the
  *   host first: on any error nothing is launched and nothing is written.
  * - Results are deterministic: identical inputs give bitwise identical
  *   outputs (no atomics on any value path).
@@ -57,14 +59,19 @@
 extern "C" {
 #endif
 
-#define WISE_ABI_VERSION 4
+#define WISE_ABI_VERSION 5
 
 typedef enum {
   WISE_OK = 0,
   WISE_ERR_INVALID_ARG = 1,  /* null pointer, bad size, eta outside (0,1], ... */
   WISE_ERR_UNSUPPORTED = 2,  /* valid but not built: head_dim or block_size    */
   WISE_ERR_CAPACITY = 3,     /* col_capacity below wise_select_max_nnz()       */
-  WISE_ERR_HIP = 4           /* the HIP runtime reported a launch error        */
+  WISE_ERR_HIP = 4,          /* the HIP runtime reported a launch error        */
+  WISE_ERR_OVERFLOW = 5      /* reserved, never returned: the kernels raise the
+                                softmax reference max whenever a score exceeds it
+                                by more than 64 (log2 units), so exp terms stay
+                                below 2^64 and no fp32 sum can overflow for
+                                supported shapes (seq_len <= 65536)           */
 } wise_status_t;
 
 /* Shape of one attention call.  All tensors of a call share it. */
@@ -90,7 +97,13 @@ typedef struct {
  *          the descriptor, heads when it is 0).
  * o:       bf16, q's layout (written, rounded to nearest even).
  * lse:     optional (NULL to skip) fp32 [batch][heads][seq_len]; receives
- *          the natural-log row normaliser log(sum_j exp(score_ij)).
+ *          the natural-log row normaliser log(sum_j exp(score_ij)).  The sum
+ *          is formed from the exp terms rounded to bf16, the same weights
+ *          that multiply V (so O is exactly the weighted mean under them);
+ *          each term then carries a relative rounding error of at most 2^-9,
+ *          and the result differs from the exact log-sum by at most
+ *          -log(1 - 2^-9) ~ 2e-3 (in practice a few 1e-4, as the roundings
+ *          of many terms cancel).
  * This is the dense baseline that the late steps are compared against.
  */
 wise_status_t wise_full_attn(const wise_attn_desc_t* desc, const void* q, const void* k,
@@ -107,7 +120,10 @@ wise_status_t wise_full_attn(const wise_attn_desc_t* desc, const void* q, const 
  *       caller zeroes it before the first discovery step; calling once per
  *       discovery step leaves the sum of r over those steps.  Entries with
  *       kb > q are never touched.  The mass reduction is fused into the
- *       attention kernel (no second pass over the attention matrix).
+ *       attention kernel, which never stores the attention matrix: one pass
+ *       over the keys while the per-(query, key block) partial sums fit in
+ *       on-chip memory, else (long rows) a first pass over the keys for the
+ *       row maxima and sums and a second that recomputes the scores.
  */
 wise_status_t wise_full_attn_accum(const wise_attn_desc_t* desc, const void* q, const void* k,
                                    const void* v, void* o, float* mass, void* stream);
@@ -149,19 +165,26 @@ int64_t wise_full_attn_accum_workspace_bytes(const wise_attn_desc_t* desc);
  *   3. k  = min(k*, max_blocks) when max_blocks > 0;
  *   4. W  = the k leading blocks, plus the sink block 0 and the diagonal
  *      block q (these two do not count toward eta or the cap).
- * Output is a CSR over rows, column indices ascending within each row:
+ * Output is a CSR over rows ("row offsets and active block indices", the
+ * format of the paper's Appendix B sparse kernels), column indices
+ * ascending within each row:
  *   row_ptr: int32 [n_rows + 1] (written; row_ptr[n_rows] = total nnz),
- *   col_idx: int32 [col_capacity] (the first row_ptr[n_rows] entries written).
+ *   col_idx: int32 [col_capacity] (the first row_ptr[n_rows] entries written),
+ *   nnz:     optional (NULL to skip) int64 on the device, 8-byte aligned;
+ *            receives the total entry count row_ptr[n_rows].  It is written
+ *            on the stream like the rest: read it after synchronising.
  *
  * mass: fp32 [batch][heads][n_blocks][n_blocks] (read; entries kb > q ignored).
- * n_steps >= 1; eta in (0, 1]; max_blocks >= 0 (0 = no cap).
+ * n_steps >= 1; eta in (0, 1] as a double (the comparisons are float64;
+ * a float eta would move the threshold, e.g. 0.9f = 0.89999998).
+ * max_blocks >= 0 (0 = no cap).
  * col_capacity must be >= wise_select_max_nnz(desc, max_blocks), else
- * WISE_ERR_CAPACITY is returned before any launch.
+ * WISE_ERR_CAPACITY is returned before any launch.  n_blocks <= 2048.
  */
 wise_status_t wise_select_support(const wise_attn_desc_t* desc, const float* mass,
                                   int32_t n_steps, double eta, int32_t max_blocks,
                                   int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
-                                  void* stream);
+                                  int64_t* nnz, void* stream);
 
 /*
  * Selection variants (same output contract as wise_select_support, no cap):
@@ -187,7 +210,7 @@ wise_status_t wise_select_support(const wise_attn_desc_t* desc, const float* mas
  * Every result then gets the sink block 0 and the diagonal block q.
  * eta in (0, 1]; col_capacity >= wise_select_max_nnz(desc, 0), else
  * WISE_ERR_CAPACITY before any launch.  Invalid kind / n_mass ->
- * WISE_ERR_INVALID_ARG.
+ * WISE_ERR_INVALID_ARG.  nnz: as in wise_select_support (optional).
  */
 typedef enum {
   WISE_SELECT_UNION = 1,
@@ -198,7 +221,7 @@ typedef enum {
 
 wise_status_t wise_select_variant(const wise_attn_desc_t* desc, int32_t kind, const float* step_mass,
                                   int32_t n_mass, double eta, int32_t* row_ptr, int32_t* col_idx,
-                                  int64_t col_capacity, void* stream);
+                                  int64_t col_capacity, int64_t* nnz, void* stream);
 
 /*
  * Reuse step, Section 5.2, Eq. (7)-(8): O = softmax(Q K^T * scale + M + R) V,
@@ -225,7 +248,8 @@ wise_status_t wise_sparse_attn(const wise_attn_desc_t* desc, const void* q, cons
 /*
  * Diagnostics of the frozen working set (Section 7, "Evaluation metrics";
  * Appendix C.2, Eq. 23-25).  CSR rows are read as sets, as in
- * wise_sparse_attn.
+ * wise_sparse_attn, with the same reading of malformed pointers (a negative
+ * start as 0, an end below the start as an empty row).
  *
  * wise_support_mass: retained[r] = sum over kb in row r's support of
  *   mass[r][kb] (float64 sum in block order, stored fp32).  With the block

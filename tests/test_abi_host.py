@@ -45,9 +45,10 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = _lib()
-    assert lib.wise_abi_version() == 4
+    assert lib.wise_abi_version() == 5
     assert lib.wise_status_string(0) == b"WISE_OK"
     assert lib.wise_status_string(3) == b"WISE_ERR_CAPACITY"
+    assert lib.wise_status_string(5) == b"WISE_ERR_OVERFLOW"
     assert lib.wise_status_string(99) == b"WISE_ERR_UNKNOWN"
 
 
@@ -90,8 +91,8 @@ def test_empty_calls_are_no_ops(b, h, s):
         assert lib.wise_full_attn_accum_workspace_bytes(r) == 0
         assert lib.wise_select_max_nnz(r, 0) == 0
         # the selection calls still need row_ptr (they write its one entry)
-        assert lib.wise_select_support(r, None, 1, 0.9, 0, None, None, 0, None) == wise.WISE_ERR_INVALID_ARG
-        assert lib.wise_select_support(r, None, 0, 0.9, 0, FAKE, None, 0, None) == wise.WISE_ERR_INVALID_ARG
+        assert lib.wise_select_support(r, None, 1, 0.9, 0, None, None, 0, None, None) == wise.WISE_ERR_INVALID_ARG
+        assert lib.wise_select_support(r, None, 0, 0.9, 0, FAKE, None, 0, None, None) == wise.WISE_ERR_INVALID_ARG
 
 
 def _status(fn, *args):
@@ -137,18 +138,22 @@ def test_select_arguments_rejected():
     assert need == 2 * sum(range(1, 9))
     # eta outside (0, 1]
     for eta in (0.0, -0.5, 1.0000001, float("nan")):
-        assert sel(ctypes.byref(d), FAKE, 2, eta, 0, FAKE, FAKE, need, None) == wise.WISE_ERR_INVALID_ARG
-    assert sel(ctypes.byref(d), FAKE, 0, 0.9, 0, FAKE, FAKE, need, None) == wise.WISE_ERR_INVALID_ARG
-    assert sel(ctypes.byref(d), FAKE, 2, 0.9, -1, FAKE, FAKE, need, None) == wise.WISE_ERR_INVALID_ARG
-    assert sel(ctypes.byref(d), None, 2, 0.9, 0, FAKE, FAKE, need, None) == wise.WISE_ERR_INVALID_ARG
-    assert sel(ctypes.byref(d), FAKE + 2, 2, 0.9, 0, FAKE, FAKE, need, None) == wise.WISE_ERR_INVALID_ARG
+        assert sel(ctypes.byref(d), FAKE, 2, eta, 0, FAKE, FAKE, need, None, None) == wise.WISE_ERR_INVALID_ARG
+    assert sel(ctypes.byref(d), FAKE, 0, 0.9, 0, FAKE, FAKE, need, None, None) == wise.WISE_ERR_INVALID_ARG
+    assert sel(ctypes.byref(d), FAKE, 2, 0.9, -1, FAKE, FAKE, need, None, None) == wise.WISE_ERR_INVALID_ARG
+    assert sel(ctypes.byref(d), None, 2, 0.9, 0, FAKE, FAKE, need, None, None) == wise.WISE_ERR_INVALID_ARG
+    assert sel(ctypes.byref(d), FAKE + 2, 2, 0.9, 0, FAKE, FAKE, need, None, None) == wise.WISE_ERR_INVALID_ARG
     # capacity below the worst case is refused before any launch
-    assert sel(ctypes.byref(d), FAKE, 2, 0.9, 0, FAKE, FAKE, need - 1, None) == wise.WISE_ERR_CAPACITY
+    assert sel(ctypes.byref(d), FAKE, 2, 0.9, 0, FAKE, FAKE, need - 1, None, None) == wise.WISE_ERR_CAPACITY
     capped = lib.wise_select_max_nnz(ctypes.byref(d), 1)
     assert capped == 2 * sum(min(q + 1, 3) for q in range(8))
-    assert sel(ctypes.byref(d), FAKE, 2, 0.9, 1, FAKE, FAKE, capped - 1, None) == wise.WISE_ERR_CAPACITY
+    assert sel(ctypes.byref(d), FAKE, 2, 0.9, 1, FAKE, FAKE, capped - 1, None, None) == wise.WISE_ERR_CAPACITY
     assert lib.wise_select_max_nnz(None, 0) == -1
     assert lib.wise_select_max_nnz(ctypes.byref(d), -3) == -1
+    # the optional device nnz output must be 8-byte aligned
+    assert sel(ctypes.byref(d), FAKE, 2, 0.9, 0, FAKE, FAKE, need, FAKE + 4, None) == wise.WISE_ERR_INVALID_ARG
+    assert lib.wise_select_variant(ctypes.byref(d), wise.SELECT_UNION, FAKE, 2, 0.9, FAKE, FAKE, need,
+                                   FAKE + 4, None) == wise.WISE_ERR_INVALID_ARG
 
 
 def test_gqa_descriptor_rejected_when_heads_do_not_split():
@@ -158,7 +163,7 @@ def test_gqa_descriptor_rejected_when_heads_do_not_split():
         d.kv_heads = kv
         assert lib.wise_full_attn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None) \
             == wise.WISE_ERR_INVALID_ARG, kv
-    assert lib.wise_abi_version() == 4
+    assert lib.wise_abi_version() == 5
 
 
 def test_select_variant_arguments_rejected():
@@ -170,21 +175,21 @@ def test_select_variant_arguments_rejected():
                    mass=(wise.SELECT_MASS_MATCHED, 5), size=(wise.SELECT_SIZE_MATCHED, 2))
     for kind, n_mass in ok_args.values():
         for eta in (0.0, 1.5, float("nan")):
-            assert sel(ctypes.byref(d), kind, FAKE, n_mass, eta, FAKE, FAKE, need, None) \
+            assert sel(ctypes.byref(d), kind, FAKE, n_mass, eta, FAKE, FAKE, need, None, None) \
                 == wise.WISE_ERR_INVALID_ARG
-        assert sel(ctypes.byref(d), kind, None, n_mass, 0.9, FAKE, FAKE, need, None) \
+        assert sel(ctypes.byref(d), kind, None, n_mass, 0.9, FAKE, FAKE, need, None, None) \
             == wise.WISE_ERR_INVALID_ARG
-        assert sel(ctypes.byref(d), kind, FAKE, n_mass, 0.9, FAKE, FAKE, need - 1, None) \
+        assert sel(ctypes.byref(d), kind, FAKE, n_mass, 0.9, FAKE, FAKE, need - 1, None, None) \
             == wise.WISE_ERR_CAPACITY
     # unknown kinds (0 is the main selection, which has its own call) and bad step counts
     for kind in (0, 5, -1):
-        assert sel(ctypes.byref(d), kind, FAKE, 2, 0.9, FAKE, FAKE, need, None) == wise.WISE_ERR_INVALID_ARG
-    assert sel(ctypes.byref(d), wise.SELECT_UNION, FAKE, 0, 0.9, FAKE, FAKE, need, None) \
+        assert sel(ctypes.byref(d), kind, FAKE, 2, 0.9, FAKE, FAKE, need, None, None) == wise.WISE_ERR_INVALID_ARG
+    assert sel(ctypes.byref(d), wise.SELECT_UNION, FAKE, 0, 0.9, FAKE, FAKE, need, None, None) \
         == wise.WISE_ERR_INVALID_ARG
-    assert sel(ctypes.byref(d), wise.SELECT_STATIC, FAKE, 2, 0.9, FAKE, FAKE, need, None) \
+    assert sel(ctypes.byref(d), wise.SELECT_STATIC, FAKE, 2, 0.9, FAKE, FAKE, need, None, None) \
         == wise.WISE_ERR_INVALID_ARG
     for kind in (wise.SELECT_MASS_MATCHED, wise.SELECT_SIZE_MATCHED):
-        assert sel(ctypes.byref(d), kind, FAKE, 1, 0.9, FAKE, FAKE, need, None) == wise.WISE_ERR_INVALID_ARG
+        assert sel(ctypes.byref(d), kind, FAKE, 1, 0.9, FAKE, FAKE, need, None, None) == wise.WISE_ERR_INVALID_ARG
 
 
 def test_binding_refuses_cpu_tensors():

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 from wise_inputs import round_to_bf16_bits
-from wise_testlib import bf16_dev_to_f64, compare_outputs, say, to_dev
+from wise_testlib import bf16_dev_to_f64, check_trajectory_rows, compare_outputs, say, to_dev
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -123,3 +123,86 @@ def test_empty_inputs_are_no_ops(shape):
     torch.cuda.synchronize()
     assert rp.cpu().tolist() == [0] and rp_u.cpu().tolist() == [0]
     assert o.shape == shape and ret.numel() == 0 and inter.numel() == 0 and uni.numel() == 0
+
+
+def test_diagnostics_malformed_row_pointers_read_in_bounds():
+    """The diagnostics read malformed CSR pointers as the sparse kernel does:
+    a negative start as 0, an end below its start as an empty row; every
+    pointer stays within col_idx once read that way."""
+    b, h, s, d, blk = 1, 2, 256, 64, 32
+    nb = s // blk
+    say("diagnostics malformed row_ptr")
+    g = np.random.default_rng(6)
+    rows = [sorted(set(g.integers(0, r % nb + 1, size=3).tolist()) | {r % nb}) for r in range(b * h * nb)]
+    rp = np.zeros(len(rows) + 1, dtype=np.int64)
+    rp[1:] = np.cumsum([len(r) for r in rows])
+    ci = np.array([x for r in rows for x in r], dtype=np.int32)
+    rp_bad = rp.copy()
+    rp_bad[0] = -5                      # row 0 reads col_idx[0:rp[1]]
+    rp_bad[4] = rp_bad[3] - 2           # row 3: end below start -> empty
+    assert rp_bad.max() <= len(ci) and rp_bad[4] >= 0
+    read = [list(ci[max(rp_bad[r], 0):max(rp_bad[r + 1], max(rp_bad[r], 0))]) for r in range(len(rows))]
+    assert read[3] == [] and read[0] == rows[0]
+    mass = np.tril(g.dirichlet(np.ones(nb), size=(b, h, nb))).astype(np.float32)
+    rp_d, ci_d = torch.from_numpy(rp_bad.astype(np.int32)).cuda(), torch.from_numpy(ci).cuda()
+    rp_ok, ci_ok = torch.from_numpy(rp.astype(np.int32)).cuda(), torch.from_numpy(ci).cuda()
+    ret = wise.wise_support_mass(torch.from_numpy(mass).cuda(), rp_d, ci_d, d, blk)
+    inter, uni = wise.wise_support_overlap((rp_d, ci_d), (rp_ok, ci_ok), b, h, nb, d, blk)
+    torch.cuda.synchronize()
+    ret, inter, uni = ret.cpu().numpy(), inter.cpu().numpy(), uni.cpu().numpy()
+    for r in range(len(rows)):
+        qb = r % nb
+        m_row = mass.reshape(-1, nb)[r].astype(np.float64)
+        want = oracle.retained_mass(m_row, read[r], qb)
+        assert abs(ret[r] - want) <= 1e-6, (r, ret[r], want)
+        a = {x for x in read[r] if 0 <= x <= qb}
+        bset = {x for x in rows[r] if 0 <= x <= qb}
+        assert (inter[r], uni[r]) == (len(a & bset), len(a | bset)), r
+
+
+def test_trajectory_on_a_side_stream():
+    """The discovery, selection (with the device nnz output) and reuse calls
+    issued on a non-default stream, with every output and the workspace
+    allocated by the binding: results equal, bit for bit, those of the same
+    calls on the current stream, and the oracle's."""
+    from wise_inputs import CONFIGS, Workload
+    cfg = CONFIGS["tiny"].with_(block=64, seq_len=512, heads=3, index=970)
+    say(f"side stream trajectory {cfg.batch}x{cfg.heads} S {cfg.seq_len} B {cfg.block}")
+    steps = list(Workload(cfg).steps())
+    nb = cfg.n_blocks
+
+    def run(stream):
+        mass = torch.zeros(cfg.batch, cfg.heads, nb, nb, dtype=torch.float32, device="cuda")
+        nnz = torch.zeros(1, dtype=torch.int64, device="cuda")
+        dev = [tuple(to_dev(x) for x in (q, k, v)) for _, q, k, v in steps]
+        if stream is not None:
+            stream.wait_stream(torch.cuda.current_stream())   # inputs are ready on the current stream
+        outs, rp, ci = [], None, None
+        for t, (q, k, v) in enumerate(dev):
+            if t < cfg.td:
+                outs.append(wise.wise_full_attn_accum_ws(q, k, v, mass, cfg.block, stream=stream))
+            else:
+                if rp is None:
+                    rp, ci = wise.wise_select_support(mass, cfg.td, cfg.eta, cfg.head_dim, cfg.block, cfg.cap,
+                                                      nnz=nnz, stream=stream)
+                outs.append(wise.wise_sparse_attn(q, k, v, rp, ci, cfg.block, stream=stream))
+        if stream is not None:
+            stream.synchronize()
+        torch.cuda.synchronize()
+        return mass.cpu(), rp.cpu(), ci.cpu(), int(nnz.cpu()), [o.cpu() for o in outs]
+
+    side = torch.cuda.Stream()
+    assert side.cuda_stream != torch.cuda.current_stream().cuda_stream
+    m0, rp0, ci0, n0, o0 = run(None)
+    m1, rp1, ci1, n1, o1 = run(side)
+    assert n0 == int(rp0[-1]) and n1 == int(rp1[-1])
+    assert torch.equal(m0, m1) and torch.equal(rp0, rp1) and torch.equal(ci0[:n0], ci1[:n1])
+    for a, b_ in zip(o0, o1):
+        assert torch.equal(a.view(torch.int16), b_.view(torch.int16))
+    rows = [ci1[rp1[r]:rp1[r + 1]].tolist() for r in range(len(rp1) - 1)]
+    outs = [oracle.bf16_to_f64(o.view(torch.int16).numpy().view(np.uint16)) for o in o1]
+    samples = [(0, h, qb) for h in range(cfg.heads) for qb in range(nb)]
+    wl = Workload(cfg)
+    stats = check_trajectory_rows(cfg, m1.numpy(), rows, lambda t, b, h, r: outs[t][b, h][r], samples,
+                                  lambda b, h: wl.head_steps(b, h, cfg.steps))
+    say(f"  {stats['rows']} rows, max-abs {stats['max_abs']:.2e}")
