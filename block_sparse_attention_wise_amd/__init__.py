@@ -24,6 +24,7 @@ from typing import Optional, Tuple
 
 __all__ = ["WiseError", "WiseDesc", "load_library", "library_path", "wise_full_attn",
            "wise_full_attn_accum", "wise_full_attn_accum_ws", "wise_accum_workspace_bytes",
+           "wise_full_attn_accum_noalloc", "wise_noalloc_max_bytes",
            "wise_select_support", "wise_select_variant", "wise_sparse_attn",
            "SELECT_UNION", "SELECT_STATIC", "SELECT_MASS_MATCHED", "SELECT_SIZE_MATCHED",
            "wise_support_mass", "wise_support_overlap",
@@ -77,6 +78,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "wise_full_attn_accum": ([dp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "wise_full_attn_accum_ws": ([dp, vp, vp, vp, vp, vp, vp, i64, vp], ctypes.c_int),
         "wise_full_attn_accum_workspace_bytes": ([dp], i64),
+        "wise_full_attn_accum_noalloc": ([dp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+        "wise_full_attn_accum_noalloc_max_bytes": ([], i64),
         "wise_select_support": ([dp, vp, i32, ctypes.c_double, i32, vp, vp, i64, vp, vp], ctypes.c_int),
         "wise_select_variant": ([dp, i32, vp, i32, ctypes.c_double, vp, vp, i64, vp, vp], ctypes.c_int),
         "wise_support_mass": ([dp, vp, vp, vp, vp, vp], ctypes.c_int),
@@ -282,6 +285,32 @@ def wise_full_attn_accum_ws(q, k, v, mass, block_size: int, o=None, workspace=No
     d = _desc(q, block_size, softmax_scale, k)
     _call("wise_full_attn_accum_ws", dev, stream, ctypes.byref(d), q.data_ptr(), k.data_ptr(),
           v.data_ptr(), o.data_ptr(), mass.data_ptr(), ws_ptr, ws_bytes)
+    return o
+
+
+def wise_noalloc_max_bytes() -> int:
+    """Size of the fixed device buffer behind wise_full_attn_accum_noalloc."""
+    return int(load_library().wise_full_attn_accum_noalloc_max_bytes())
+
+
+def wise_full_attn_accum_noalloc(q, k, v, mass, block_size: int, o, softmax_scale: float = 0.0, stream=None):
+    """Discovery step as wise_full_attn_accum_ws, with the block-mass partials
+    in the library's fixed per-GPU buffer: no device memory is allocated,
+    here or in the library (``o`` must therefore be given).  Calls on one
+    GPU that overlap in time race on that buffer."""
+    torch = _torch()
+    block_size = _block(block_size)
+    _qkv(q, k, v)
+    _need(mass, "mass", torch.float32, 4)
+    if tuple(mass.shape) != _mass_shape(q, block_size):
+        raise ValueError(f"mass must be {_mass_shape(q, block_size)}, got {tuple(mass.shape)}")
+    if o is None:
+        raise ValueError("o must be given: this call allocates nothing")
+    o = _out(o, q)
+    dev = _same_device((q, "q"), (k, "k"), (v, "v"), (o, "o"), (mass, "mass"))
+    d = _desc(q, block_size, softmax_scale, k)
+    _call("wise_full_attn_accum_noalloc", dev, stream, ctypes.byref(d), q.data_ptr(), k.data_ptr(),
+          v.data_ptr(), o.data_ptr(), mass.data_ptr())
     return o
 
 

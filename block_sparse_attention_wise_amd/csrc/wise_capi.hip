@@ -1,6 +1,7 @@
 // C ABI of libwise (declared in include/wise.h): host-side validation and
 // dispatch to the HIP kernels.  Validation is pure host code and touches no
 // device state, so invalid calls return before anything is launched.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -158,6 +159,39 @@ int64_t max_nnz(int32_t nblk, int64_t heads_total, int32_t max_blocks) {
   return per_head * heads_total;
 }
 
+// Fixed device buffer of wise_full_attn_accum_noalloc: the block-mass
+// partials of the workspace launch for callers that cannot allocate.  Every
+// GPU the library runs on holds one copy for the life of the process.  In
+// host code `scratch` names a host-side stand-in, not device memory: the
+// kernels only ever receive the device address that hipGetSymbolAddress
+// reports for the current device, kept per device below.
+constexpr int64_t kScratchBytes = 64ll << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kScratchDevices];   // per device; null until first looked up
+
+// Device address of `scratch` on the current device (looked up once per
+// device; concurrent first calls may both look it up and store the same
+// value).  Returns nullptr and sets the error text on failure.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) {
+    fail(WISE_ERR_HIP, "no usable current device for the scratch buffer");
+    return nullptr;
+  }
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      fail(WISE_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
+
 }  // namespace
 }  // namespace wise
 
@@ -202,6 +236,32 @@ wise_status_t wise_full_attn_accum_ws(const wise_attn_desc_t* desc, const void* 
   return run_attn(desc, kDenseMassWs, q, k, v, o, nullptr, mass, nullptr, nullptr, stream,
                   static_cast<float*>(workspace));
 }
+
+wise_status_t wise_full_attn_accum_noalloc(const wise_attn_desc_t* desc, const void* q, const void* k,
+                                           const void* v, void* o, float* mass, void* stream) {
+  int32_t nblk;
+  int64_t n_rows;
+  wise_status_t st = check_desc(desc, &nblk, &n_rows);
+  if (st != WISE_OK) return st;
+  const int64_t need = accum_workspace_bytes(desc, nblk, n_rows);
+  if (need == 0) return run_attn(desc, kDenseMass, q, k, v, o, nullptr, mass, nullptr, nullptr, stream);
+  if (need > kScratchBytes)
+    return fail(WISE_ERR_CAPACITY, "this call needs %lld bytes of block-mass partials; the fixed buffer "
+                "holds %lld (batch * heads * n_blocks^2 * block_size * 4 must not exceed it)",
+                (long long)need, (long long)kScratchBytes);
+  // Validate the caller's arguments before the first device call.
+  if ((st = check_tensor(q, "q")) != WISE_OK) return st;
+  if ((st = check_tensor(k, "k")) != WISE_OK) return st;
+  if ((st = check_tensor(v, "v")) != WISE_OK) return st;
+  if ((st = check_tensor(o, "o")) != WISE_OK) return st;
+  if (mass == nullptr) return fail(WISE_ERR_INVALID_ARG, "mass is NULL");
+  void* ws = scratch_ptr();
+  if (ws == nullptr) return WISE_ERR_HIP;
+  return run_attn(desc, kDenseMassWs, q, k, v, o, nullptr, mass, nullptr, nullptr, stream,
+                  static_cast<float*>(ws));
+}
+
+int64_t wise_full_attn_accum_noalloc_max_bytes(void) { return kScratchBytes; }
 
 wise_status_t wise_sparse_attn(const wise_attn_desc_t* desc, const void* q, const void* k, const void* v,
                                const int32_t* row_ptr, const int32_t* col_idx, void* o, void* stream) {

@@ -150,6 +150,32 @@ wise_status_t wise_full_attn_accum_ws(const wise_attn_desc_t* desc, const void* 
                                       const void* v, void* o, float* mass, void* workspace,
                                       int64_t workspace_bytes, void* stream);
 
+/*
+ * wise_full_attn_accum_ws without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  The per-(query, key
+ * block) partials live in a fixed buffer of
+ * wise_full_attn_accum_noalloc_max_bytes() bytes (64 MiB) that the library
+ * holds in each GPU's memory for the life of the process; the call itself
+ * allocates nothing.  Same kernels, arguments and results as
+ * wise_full_attn_accum_ws (bitwise).
+ *
+ * Limit: wise_full_attn_accum_workspace_bytes(desc) must not exceed the
+ * buffer (for example 32 heads x 4096 keys at block 64 need 32 MiB), else
+ * WISE_ERR_CAPACITY with nothing launched.  Block sizes 16 and 32 need no
+ * buffer and run wise_full_attn_accum.
+ * Nothing in the buffer must start at zero: every partial is written before
+ * it is read.  All calls on one GPU share its buffer, so two calls that
+ * overlap in time on that GPU (on different streams, or from different host
+ * threads without ordering) race on it; the caller orders them.  The first
+ * call on a device looks up the buffer's device address (no allocation).
+ */
+wise_status_t wise_full_attn_accum_noalloc(const wise_attn_desc_t* desc, const void* q, const void* k,
+                                           const void* v, void* o, float* mass, void* stream);
+
+/* Size in bytes of the fixed buffer of wise_full_attn_accum_noalloc. */
+int64_t wise_full_attn_accum_noalloc_max_bytes(void);
+
 /* Workspace bytes wise_full_attn_accum_ws needs for this descriptor:
  * batch * heads * n_blocks^2 * block_size * 4 for block sizes 64 and 128,
  * 0 for 16 and 32; -1 for an invalid descriptor. */

@@ -265,3 +265,22 @@ def test_accum_workspace_size_and_arguments():
     # mass is still required
     assert f(ctypes.byref(d), FAKE, FAKE, FAKE, O, None, FAKE << 8, need, None) == wise.WISE_ERR_INVALID_ARG
     assert lib.wise_last_error() != b""
+
+
+def test_noalloc_call_refuses_sizes_beyond_its_buffer():
+    """wise_full_attn_accum_noalloc checks its fixed buffer's limit and its
+    arguments on the host, before any device call."""
+    lib = _lib()
+    assert lib.wise_full_attn_accum_noalloc_max_bytes() == 64 << 20
+    big = wise.WiseDesc(1, 65, 4096, 128, 64, 0.0)
+    assert lib.wise_full_attn_accum_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE + 4096, FAKE, None) \
+        == wise.WISE_ERR_CAPACITY
+    fits = wise.WiseDesc(1, 64, 4096, 128, 64, 0.0)
+    assert lib.wise_full_attn_accum_workspace_bytes(ctypes.byref(fits)) == 64 << 20
+    assert lib.wise_full_attn_accum_noalloc(ctypes.byref(fits), None, FAKE, FAKE, FAKE, FAKE, None) \
+        == wise.WISE_ERR_INVALID_ARG
+    assert lib.wise_full_attn_accum_noalloc(ctypes.byref(fits), FAKE, FAKE, FAKE, FAKE + 4096, None, None) \
+        == wise.WISE_ERR_INVALID_ARG
+    empty = wise.WiseDesc(0, 4, 4096, 128, 64, 0.0)
+    assert lib.wise_full_attn_accum_noalloc(ctypes.byref(empty), None, None, None, None, None, None) \
+        == wise.WISE_OK
