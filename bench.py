@@ -8,9 +8,17 @@ block-sparse attention, each step on its own synthetic Q/K/V already resident
 in HBM.  The headline value is the late-step block-sparse kernel's throughput
 on its executed MFMA FLOPs; the same run reports the late-step speedup over
 the library's own dense kernel, the realised support density, a roofline
-record for the sparse kernel and the fp64 CPU oracle timed on a sample.
+record for the sparse kernel and the fp64 CPU oracle timed on a sample
+(discovery, selection and late phases, plus a single-thread sample).
 
-    python bench.py [--steps K] [--warmup W] [--config ctx4k] [--no-cpu-baseline]
+A sweep over the other workloads (8K, 16K and 32K context, the wide-head
+batched workload and the long block-128 workload) follows, each with its own
+discovery steps, selection and a few reuse steps: late-step TFLOP/s, the
+fraction of the bf16 peak, speedup over the dense kernel next to
+1/density, and the same-backend comparison, every timing as median and
+interquartile range.
+
+    python bench.py [--steps K] [--warmup W] [--config ctx4k] [--no-cpu-baseline] [--no-sweep]
 """
 from __future__ import annotations
 
@@ -41,15 +49,21 @@ def parse(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="ctx4k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--cpu-heads", type=int, default=4, help="most heads in the CPU-oracle sample")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of timed CPU-oracle work")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the per-workload sweep (8K, 16K, 32K, wide, long)")
+    ap.add_argument("--sweep", default="ctx8k,ctx16k,ctx32k,wide,long",
+                    help="workloads of the sweep (comma-separated)")
+    ap.add_argument("--sweep-passes", type=int, default=7)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB first (HBM counter calibration)")
     ap.add_argument("--no-block-study", action="store_true",
                     help="skip the block-size study (the same inputs at block 16, 32, 64, 128)")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the selection-variant figures (temporal union and the early-static controls)")
-    ap.add_argument("--same-backend", action="store_true",
-                    help="also time the sparse kernel on a full causal CSR")
+    ap.add_argument("--no-same-backend", action="store_true",
+                    help="skip timing the sparse kernel on a full causal CSR (the same-backend comparison)")
     return ap.parse_args(argv)
 
 
@@ -121,48 +135,220 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(cfg, n_heads: int):
-    """The fp64 oracle, as it stands, on a bounded sample: the first
-    ``n_heads`` heads of the workload, each through td dense steps, the
-    selection and all T - td late steps.  Only the late steps are timed; the
-    rate uses the same algorithmic FLOP count as the GPU figure, restricted to
-    the sample."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, max_heads: int, budget_s: float = 20.0):
+    """The fp64 oracle, as it stands, timed on a bounded sample of the
+    workload: heads 0, 1, ... of batch 0, each through its td discovery steps
+    (dense attention, Eq. 2, with the block mass of Eq. 5), the selection
+    (Eq. 6 on the mean mass) and its T - td late steps (masked attention,
+    Eq. 8), until ``max_heads`` heads or about ``budget_s`` seconds of timed
+    work.  Each phase is timed on its own.  The headline rate is the late
+    phase's, on the same algorithmic FLOP count as the GPU figure; one
+    discovery and one late head-step are also timed on a single thread."""
     import oracle
     from wise_inputs import Workload
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:                                          # pragma: no cover
+        threadpool_limits = None
         threads = os.cpu_count() or 1
     wl = Workload(cfg, threads=1)
-    B, td = cfg.block, cfg.td
-    sc = oracle.default_scale(cfg.head_dim)
-    t_late, flops, n_late = 0.0, 0.0, 0
-    for h in range(n_heads):
+    B, td, D, S, nb = cfg.block, cfg.td, cfg.head_dim, cfg.seq_len, cfg.n_blocks
+    sc = oracle.default_scale(D)
+    dense_flops = 4.0 * D * S * (S + 1) / 2                    # one head, one step, algorithmic
+
+    def discovery(Q, K, V):
+        a = oracle.attention_weights(Q, K, sc)
+        oracle.attention_output(a, V)
+        return np.array([oracle.block_mass_rows(a[oracle.block_rows(qb, B, S)], B) for qb in range(nb)])
+
+    def late_flops(supports):
+        n_pairs = 0
+        for qb, sup in supports.items():
+            n_pairs += B * B * (len(sup) - 1) + B * (B + 1) // 2
+        return 4.0 * D * n_pairs
+
+    t_disc = t_sel = t_late = 0.0
+    n_disc = n_sel = n_late = 0
+    f_late = 0.0
+    first = None
+    for h in range(max_heads):
         masses, supports = [], {}
         for t, (q, k, v) in wl.head_steps(0, h):
             Q, K, V = (oracle.bf16_to_f64(x) for x in (q, k, v))
             if t < td:
-                masses.append(oracle.block_mass(Q, K, sc, B))
+                t0 = time.perf_counter()
+                masses.append(discovery(Q, K, V))
+                t_disc += time.perf_counter() - t0
+                n_disc += 1
                 continue
             if not supports:
+                t0 = time.perf_counter()
                 mbar = oracle.mean_block_mass(masses)
-                supports = {qb: oracle.select_support(mbar[qb], qb, cfg.eta, cfg.cap)
-                            for qb in range(cfg.n_blocks)}
+                supports = {qb: oracle.select_support(mbar[qb], qb, cfg.eta, cfg.cap) for qb in range(nb)}
+                t_sel += time.perf_counter() - t0
+                n_sel += 1
+            if first is None:
+                first = (Q, K, V, supports, masses[-1])
             t0 = time.perf_counter()
             oracle.masked_attention(Q, K, V, supports, B, sc)
             t_late += time.perf_counter() - t0
             n_late += 1
-            n_pairs = 0
-            for qb, sup in supports.items():
-                n_pairs += B * B * (len(sup) - 1) + B * (B + 1) // 2
-            flops += 4.0 * cfg.head_dim * n_pairs
-    return {"value": flops / t_late / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            f_late += late_flops(supports)
+            if t_disc + t_sel + t_late > budget_s:
+                break
+        if t_disc + t_sel + t_late > budget_s:
+            break
+    single = None
+    if threadpool_limits is not None and first is not None:
+        Q, K, V, supports, _ = first
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            discovery(Q, K, V)
+            t1 = time.perf_counter()
+            oracle.masked_attention(Q, K, V, supports, B, sc)
+            t2 = time.perf_counter()
+        single = {"threads": 1, "discovery_tflops": round(dense_flops / (t1 - t0) / 1e12, 5),
+                  "late_tflops": round(late_flops(supports) / (t2 - t1) / 1e12, 5),
+                  "discovery_s_per_head_step": round(t1 - t0, 3), "late_s_per_head_step": round(t2 - t1, 3)}
+    return {"value": f_late / t_late / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": (f"heads 0..{n_heads - 1} of batch 0 of {cfg.name}: {td} dense discovery "
-                       f"steps + selection each, then {n_late} late masked-attention head-steps "
-                       f"timed ({t_late:.1f} s); algorithmic FLOPs of the sample's supports"),
-            "host_cpus": os.cpu_count()}
+            "sample": (f"batch 0, heads 0..{n_sel - 1} of {cfg.name} (of {cfg.batch * cfg.heads}): "
+                       f"{n_disc} discovery head-steps, {n_sel} selections, {n_late} late head-steps, "
+                       f"each phase timed ({t_disc:.1f} + {t_sel:.2f} + {t_late:.1f} s); value = late "
+                       f"phase on the algorithmic FLOPs of the sample's supports"),
+            "phases": {"discovery_tflops": round(n_disc * dense_flops / t_disc / 1e12, 5) if n_disc else None,
+                       "discovery_s_per_head_step": round(t_disc / max(n_disc, 1), 3),
+                       "select_ms_per_head": round(1e3 * t_sel / max(n_sel, 1), 2),
+                       "late_tflops": round(f_late / t_late / 1e12, 5),
+                       "late_s_per_head_step": round(t_late / max(n_late, 1), 3)},
+            "single_thread": single,
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "threads_note": "BLAS calls use `cores` threads; numpy's elementwise steps run on one"}
+
+
+def quartiles(xs):
+    """Median and interquartile range of a list of timings."""
+    q25, q50, q75 = np.percentile(np.asarray(xs, dtype=np.float64), [25, 50, 75])
+    return {"median": round(float(q50), 4), "iqr": [round(float(q25), 4), round(float(q75), 4)]}
+
+
+def run_sweep(names, passes, wise, torch, dev, n_late=4):
+    """Per-workload figures on one GPU: for each workload, its td discovery
+    steps (dense attention + fused block mass, workspace partials), the
+    selection, and n_late reuse steps on their own drifted inputs; the
+    sparse launch is timed against the library's dense launch on the same
+    late-step inputs and against itself on a full causal CSR (the
+    same-backend comparison).  Every timing is the per-launch average of one
+    pass of back-to-back launches, over ``passes`` passes (median and IQR)."""
+    from wise_inputs import CONFIGS, Workload
+    out = {}
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n_launch, reps):
+        fn()                                   # warm-up pass
+        xs = []
+        for _ in range(reps):
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            xs.append(e0.elapsed_time(e1) / n_launch)
+        return xs
+
+    for name in names:
+        cfg = CONFIGS[name]
+        td, T, B, D, nb = cfg.td, cfg.steps, cfg.block, cfg.head_dim, cfg.n_blocks
+        n_steps = td + n_late
+        log(f"sweep {name}: generating {n_steps} steps")
+        t0 = time.time()
+        qs, ks, vs = [], [], []
+        for t, q, k, v in Workload(cfg, threads=min(16, os.cpu_count() or 1)).steps(n_steps):
+            for src, dst in ((q, qs), (k, ks), (v, vs)):
+                dst.append(torch.from_numpy(src.view(np.int16)).view(torch.bfloat16).to(dev))
+        log(f"sweep {name}: inputs ready in {time.time() - t0:.1f} s")
+        mass = torch.zeros(cfg.batch, cfg.heads, nb, nb, dtype=torch.float32, device=dev)
+        o = torch.empty_like(qs[0])
+        ws = torch.empty(max(wise.wise_accum_workspace_bytes(cfg.batch, cfg.heads, cfg.seq_len, D, B), 16),
+                         dtype=torch.uint8, device=dev)
+        n_rows = cfg.batch * cfg.heads * nb
+        row_ptr = torch.empty(n_rows + 1, dtype=torch.int32, device=dev)
+        col_idx = torch.empty(wise.wise_select_max_nnz(cfg.batch, cfg.heads, cfg.seq_len, D, B, cfg.cap),
+                              dtype=torch.int32, device=dev)
+
+        def discover():
+            mass.zero_()
+            for t in range(td):
+                wise.wise_full_attn_accum_ws(qs[t], ks[t], vs[t], mass, B, o=o, workspace=ws)
+
+        def select():
+            wise.wise_select_support(mass, td, cfg.eta, D, B, cfg.cap, row_ptr=row_ptr, col_idx=col_idx)
+
+        k1 = timed(discover, td, passes)
+        discover()
+        k3 = timed(select, 1, passes)
+        rp_h = row_ptr.cpu().numpy()
+        fc = flop_counts(cfg, rp_h)
+
+        def late():
+            for t in range(td, n_steps):
+                wise.wise_sparse_attn(qs[t], ks[t], vs[t], row_ptr, col_idx, B, o=o)
+
+        def dense():
+            for t in range(td, n_steps):
+                wise.wise_full_attn(qs[t], ks[t], vs[t], B, o=o)
+        full_rp = torch.from_numpy(np.concatenate([[0], np.cumsum(
+            np.tile(np.arange(1, nb + 1), cfg.batch * cfg.heads))]).astype(np.int32)).to(dev)
+        full_ci = torch.from_numpy(np.tile(np.concatenate([np.arange(q + 1) for q in range(nb)]),
+                                           cfg.batch * cfg.heads).astype(np.int32)).to(dev)
+
+        def full():
+            for t in range(td, n_steps):
+                wise.wise_sparse_attn(qs[t], ks[t], vs[t], full_rp, full_ci, B, o=o)
+        k4 = timed(late, n_late, passes)
+        k2 = timed(dense, n_late, passes)
+        kf = timed(full, n_late, max(3, passes // 2))
+        m = lambda xs: float(np.median(xs))
+        t4, t2, t1, t3, tf = m(k4), m(k2), m(k1), m(k3), m(kf)
+        ideal = 1.0 / fc["density_adm"]
+        out[name] = {
+            "workload": (f"batch {cfg.batch}, {cfg.heads} heads, head_dim {D}, seq {cfg.seq_len}, block {B}, "
+                         f"T {T}, td {td}, eta {cfg.eta}, cap {cfg.cap}"),
+            "density_admissible": round(fc["density_adm"], 4),
+            "density_full_grid": round(fc["density_full"], 4),
+            "sparse_tflops_exec": round(fc["sparse_exec"] / (t4 * 1e-3) / 1e12, 2),
+            "frac_bf16_peak_algorithmic": round(fc["sparse_alg"] / (t4 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "late_step_speedup_vs_dense": round(t2 / t4, 3),
+            "ideal_speedup_1_over_density": round(ideal, 3),
+            "speedup_over_ideal": round(t2 / t4 / ideal, 3),
+            "same_backend_full_vs_support": round(tf / t4, 3),
+            "setup_inclusive_speedup": round((T - td) * t2 / (t3 + (T - td) * t4), 3),
+            "trajectory_speedup": round(T * t2 / (td * t1 + t3 + (T - td) * t4), 3),
+            "dense_tflops_exec": round(fc["dense_exec"] / (t2 * 1e-3) / 1e12, 2),
+            "accum_tflops_exec": round(fc["dense_exec"] / (t1 * 1e-3) / 1e12, 2),
+            "kernel_ms": {"sparse_attn": quartiles(k4), "full_attn": quartiles(k2),
+                          "full_attn_accum": quartiles(k1), "select_support": quartiles(k3),
+                          "sparse_attn_full_csr": quartiles(kf)},
+            "timed": f"{passes} passes of {n_late} late / {td} discovery launches; trajectory figures "
+                     f"use the workload's T {T} and td {td} with these per-launch times",
+        }
+        log(f"sweep {name}: sparse {out[name]['sparse_tflops_exec']} TFLOP/s, speedup "
+            f"{out[name]['late_step_speedup_vs_dense']} (ideal {out[name]['ideal_speedup_1_over_density']})")
+        del qs, ks, vs, mass, o, ws, row_ptr, col_idx, full_rp, full_ci
+        torch.cuda.empty_cache()
+    return out
 
 
 def main(argv=None):
@@ -278,7 +464,7 @@ def main(argv=None):
     def full_sparse():
         for t in range(td, T):
             wise.wise_sparse_attn(qs[t], ks[t], vs[t], full_rp, full_ci, B, o=outs[t])
-    if args.same_backend:
+    if not args.no_same_backend:
         for _ in range(args.warmup):
             full_sparse()
         for _ in range(max(3, args.steps // 4)):
@@ -410,6 +596,13 @@ def main(argv=None):
         "kernel_ms": {"sparse_attn": round(k4_ms, 4), "full_attn_accum": round(k1_ms, 4),
                       "select_support": round(k3_ms, 4), "full_attn": round(k2_ms, 4),
                       "sparse_attn_full_csr": round(kfull_ms, 4) if kfull_ms else None},
+        "kernel_ms_quartiles": {"sparse_attn": quartiles([x / n_late for x in per["k4"]]),
+                                "full_attn_accum": quartiles([x / td for x in per["k1"]]),
+                                "select_support": quartiles(per["k3"]),
+                                "full_attn": quartiles([x / n_late for x in dts]),
+                                "sparse_attn_full_csr": quartiles([x / n_late for x in fts]) if fts else None,
+                                "note": "per launch: each timed trajectory's launches back to back, "
+                                        "median and interquartile range over the timed trajectories"},
         "dense_tflops_exec": round(fc["dense_exec"] / (k2_ms * 1e-3) / 1e12, 2),
         "accum_tflops_exec": round(fc["dense_exec"] / (k1_ms * 1e-3) / 1e12, 2),
         "sparse_tflops_algorithmic": round(alg_tflops, 2),
@@ -461,9 +654,14 @@ def main(argv=None):
         result["diagnostics"] = diagnostics
     if block_study is not None:
         result["block_size_study"] = block_study
+    if not args.no_sweep:
+        del qs, ks, vs, outs
+        torch.cuda.empty_cache()
+        names = [n for n in args.sweep.split(",") if n and n != args.config]
+        result["sweep"] = run_sweep(names, args.sweep_passes, wise, torch, dev)
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a sample (cpu_baseline)")
-        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_heads)
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_heads, args.cpu_budget)
     print(json.dumps(result), flush=True)
 
 
