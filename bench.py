@@ -3,7 +3,9 @@
 One timed step is one whole recurrent-attention trajectory of the 4K
 workload (batch 1, 32 heads, head_dim 128, seq 4096, block 64, T = 32
 recurrent steps, td = 8, eta = 0.9): td discovery steps (dense attention +
-fused block mass), one support selection, and T - td reuse steps of
+fused block mass, in whichever of its two forms - partials on chip or in a
+workspace - is faster on the workload), one support selection, and T - td
+reuse steps of
 block-sparse attention, each step on its own synthetic Q/K/V already resident
 in HBM.  The headline value is the late-step block-sparse kernel's throughput
 on its executed MFMA FLOPs; the same run reports the late-step speedup over
@@ -238,6 +240,37 @@ def cpu_baseline(cfg, max_heads: int, budget_s: float = 20.0):
             "threads_note": "BLAS calls use `cores` threads; numpy's elementwise steps run on one"}
 
 
+def discovery_forms(wise, torch, cfg, qs, ks, vs, mass, ws, o, reps=3):
+    """Both forms of the discovery step (dense attention + fused block mass,
+    Eq. 2 and 5) on the workload's td discovery inputs: the one with the
+    per-(query, key block) partials on chip (wise_full_attn_accum: LDS, or a
+    second pass over the keys for long rows) and the one with them in a
+    device workspace (wise_full_attn_accum_ws).  Returns per-launch ms of
+    each (median over ``reps`` passes) and the faster form's name."""
+    td, B = cfg.td, cfg.block
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    forms = {
+        "on_chip": lambda t: wise.wise_full_attn_accum(qs[t], ks[t], vs[t], mass, B, o=o),
+        "workspace": lambda t: wise.wise_full_attn_accum_ws(qs[t], ks[t], vs[t], mass, B, o=o, workspace=ws),
+    }
+    out = {}
+    for name, fn in forms.items():
+        xs = []
+        for r in range(reps + 1):
+            mass.zero_()
+            e0.record(stream)
+            for t in range(td):
+                fn(t)
+            e1.record(stream)
+            e1.synchronize()
+            if r > 0:
+                xs.append(e0.elapsed_time(e1) / td)
+        out[name] = float(np.median(xs))
+    mass.zero_()
+    return out, min(out, key=out.get)
+
+
 def quartiles(xs):
     """Median and interquartile range of a list of timings."""
     q25, q50, q75 = np.percentile(np.asarray(xs, dtype=np.float64), [25, 50, 75])
@@ -288,10 +321,15 @@ def run_sweep(names, passes, wise, torch, dev, n_late=4):
         col_idx = torch.empty(wise.wise_select_max_nnz(cfg.batch, cfg.heads, cfg.seq_len, D, B, cfg.cap),
                               dtype=torch.int32, device=dev)
 
+        forms, used = discovery_forms(wise, torch, cfg, qs, ks, vs, mass, ws, o)
+
         def discover():
             mass.zero_()
             for t in range(td):
-                wise.wise_full_attn_accum_ws(qs[t], ks[t], vs[t], mass, B, o=o, workspace=ws)
+                if used == "on_chip":
+                    wise.wise_full_attn_accum(qs[t], ks[t], vs[t], mass, B, o=o)
+                else:
+                    wise.wise_full_attn_accum_ws(qs[t], ks[t], vs[t], mass, B, o=o, workspace=ws)
 
         def select():
             wise.wise_select_support(mass, td, cfg.eta, D, B, cfg.cap, row_ptr=row_ptr, col_idx=col_idx)
@@ -338,6 +376,8 @@ def run_sweep(names, passes, wise, torch, dev, n_late=4):
             "trajectory_speedup": round(T * t2 / (td * t1 + t3 + (T - td) * t4), 3),
             "dense_tflops_exec": round(fc["dense_exec"] / (t2 * 1e-3) / 1e12, 2),
             "accum_tflops_exec": round(fc["dense_exec"] / (t1 * 1e-3) / 1e12, 2),
+            "discovery_forms": {n: {"ms": round(v, 4), "tflops_exec": round(fc["dense_exec"] / (v * 1e-3) / 1e12, 2)}
+                                for n, v in forms.items()} | {"used": used},
             "kernel_ms": {"sparse_attn": quartiles(k4), "full_attn": quartiles(k2),
                           "full_attn_accum": quartiles(k1), "select_support": quartiles(k3),
                           "sparse_attn_full_csr": quartiles(kf)},
@@ -388,17 +428,28 @@ def main(argv=None):
     col_idx = torch.empty(cap, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    # Discovery steps keep their block-mass partials in a device workspace
-    # (allocated once, outside the timed region).
+    # Workspace of the discovery step's workspace form (allocated once,
+    # outside the timed region).
     ws = torch.empty(max(wise.wise_accum_workspace_bytes(cfg.batch, cfg.heads, cfg.seq_len, D, B), 16),
                      dtype=torch.uint8, device=dev)
+
+    # The discovery step runs in whichever of its two forms is faster on this
+    # workload (on-chip partials, or partials in the workspace).
+    forms, used_form = discovery_forms(wise, torch, cfg, qs, ks, vs, mass, ws, outs[0])
+    log(f"discovery forms (ms per launch): {forms}; trajectory uses {used_form}")
+
+    def accum(t, m):
+        if used_form == "on_chip":
+            wise.wise_full_attn_accum(qs[t], ks[t], vs[t], m, B, o=outs[t])
+        else:
+            wise.wise_full_attn_accum_ws(qs[t], ks[t], vs[t], m, B, o=outs[t], workspace=ws)
 
     def trajectory(record=False):
         if record:
             ev[0].record(stream)
         mass.zero_()
         for t in range(td):
-            wise.wise_full_attn_accum_ws(qs[t], ks[t], vs[t], mass, B, o=outs[t], workspace=ws)
+            accum(t, mass)
         if record:
             ev[1].record(stream)
         wise.wise_select_support(mass, td, cfg.eta, D, B, cfg.cap, row_ptr=row_ptr, col_idx=col_idx)
@@ -498,7 +549,7 @@ def main(argv=None):
     if not args.no_variants:
         step_mass = torch.zeros(td, cfg.batch, cfg.heads, nb, nb, dtype=torch.float32, device=dev)
         for t in range(td):
-            wise.wise_full_attn_accum_ws(qs[t], ks[t], vs[t], step_mass[t], B, o=outs[t], workspace=ws)
+            accum(t, step_mass[t])
         win = step_mass[td - min(4, td):td].contiguous()
         first = step_mass[:1].contiguous()
         ctrl = torch.cat([first, win]).contiguous()
@@ -530,7 +581,7 @@ def main(argv=None):
         # switch (Eq. 24) and the switch-vs-final Jaccard (Eq. 25).
         late_mass = torch.zeros(T - td, cfg.batch, cfg.heads, nb, nb, dtype=torch.float32, device=dev)
         for t in range(td, T):
-            wise.wise_full_attn_accum_ws(qs[t], ks[t], vs[t], late_mass[t - td], B, o=outs[t], workspace=ws)
+            accum(t, late_mass[t - td])
         sel_union = wise.wise_select_variant(wise.SELECT_UNION, win, cfg.eta, D, B)
 
         def retained(csr):
@@ -605,6 +656,8 @@ def main(argv=None):
                                         "median and interquartile range over the timed trajectories"},
         "dense_tflops_exec": round(fc["dense_exec"] / (k2_ms * 1e-3) / 1e12, 2),
         "accum_tflops_exec": round(fc["dense_exec"] / (k1_ms * 1e-3) / 1e12, 2),
+        "discovery_forms": {n: {"ms": round(v, 4), "tflops_exec": round(fc["dense_exec"] / (v * 1e-3) / 1e12, 2)}
+                            for n, v in forms.items()} | {"used": used_form},
         "sparse_tflops_algorithmic": round(alg_tflops, 2),
         "roofline": {"bound": "mfma", "kernel": f"wise_attn_kernel (sparse, head_dim {D}, block {B})",
                      "achieved": round(alg_tflops, 2), "peak": PEAK_BF16_TFLOPS,

@@ -1109,6 +1109,14 @@ hipError_t launch_attn_t(const AttnParams& p_in, hipStream_t stream) {
   p.head_chunk = choose_head_chunk(dev, p.heads_total, n_groups,
                                    std::max(1, std::min(regs_wgs, (int)(kMaxLds / std::max<size_t>(lds, 1)))));
   const unsigned grid = (unsigned)p.heads_total * (unsigned)n_groups;
+  if (trace_enabled()) {
+    static const char* const kModeName[] = {"dense", "dense+mass", "sparse", "mass two-pass", "dense+mass ws"};
+    trace_launch("wise_attn_kernel", grid, Sh::kThreads, lds,
+                 "mode=%s head_dim=%d block=%d keys_per_tile=%d rows_per_wg=%d logical_per_row=%d seq=%d "
+                 "n_blocks=%d heads=%d kv_group=%d head_chunk=%d wgs_per_cu_by_registers=%d",
+                 kModeName[MODE], D, BLK / LPR, KT, RPW, LPR, p.seq, p.nblk * LPR, p.heads_total, p.kv_group,
+                 p.head_chunk, regs_wgs);
+  }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(Sh::kThreads), lds, stream, p);
   return hipGetLastError();
 }

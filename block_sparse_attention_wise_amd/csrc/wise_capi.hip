@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "../../include/wise.h"
@@ -32,6 +33,23 @@ hipError_t launch_attn(const AttnLaunch& cfg, const AttnParams& p, hipStream_t s
     case 128: return launch_attn_d128(cfg.block, cfg.mode, p, stream);
   }
   return hipErrorInvalidValue;
+}
+
+bool trace_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("WISE_TRACE");
+    return v != nullptr && v[0] != '\0' && std::strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+void trace_launch(const char* kernel, unsigned grid, unsigned threads, size_t lds, const char* fmt, ...) {
+  char detail[192];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(detail, sizeof(detail), fmt, ap);
+  va_end(ap);
+  std::fprintf(stderr, "[wise] %s grid=%u threads=%u lds=%zu %s\n", kernel, grid, threads, lds, detail);
 }
 
 namespace {

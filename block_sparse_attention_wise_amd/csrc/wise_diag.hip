@@ -97,6 +97,7 @@ hipError_t launch_support_mass(const float* mass, const int32_t* row_ptr, const 
                                int n_rows, int nblk, hipStream_t stream) {
   if (nblk > 64 * kMaxWords) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)((n_rows + kDiagWaves - 1) / kDiagWaves);
+  if (trace_enabled()) trace_launch("support_mass_kernel", grid, 64 * kDiagWaves, 0, "rows=%d n_blocks=%d", n_rows, nblk);
   hipLaunchKernelGGL(support_mass_kernel, dim3(grid), dim3(64 * kDiagWaves), 0, stream, mass, row_ptr, col_idx,
                      out, n_rows, nblk);
   return hipGetLastError();
@@ -107,6 +108,8 @@ hipError_t launch_support_overlap(const int32_t* rp_a, const int32_t* ci_a, cons
                                   hipStream_t stream) {
   if (nblk > 64 * kMaxWords) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)((n_rows + kDiagWaves - 1) / kDiagWaves);
+  if (trace_enabled())
+    trace_launch("support_overlap_kernel", grid, 64 * kDiagWaves, 0, "rows=%d n_blocks=%d", n_rows, nblk);
   hipLaunchKernelGGL(support_overlap_kernel, dim3(grid), dim3(64 * kDiagWaves), 0, stream, rp_a, ci_a, rp_b,
                      ci_b, inter, uni, n_rows, nblk);
   return hipGetLastError();

@@ -90,4 +90,11 @@ hipError_t launch_support_overlap(const int32_t* rp_a, const int32_t* ci_a, cons
 // LDS budget of one workgroup on gfx950.
 constexpr size_t kMaxLds = 160 * 1024;
 
+// Per-launch trace on stderr when the environment sets WISE_TRACE to a
+// non-empty value other than "0" (read once per process): kernel, grid,
+// workgroup size, dynamic LDS and launch parameters, one line per launch.
+bool trace_enabled();
+void trace_launch(const char* kernel, unsigned grid, unsigned threads, size_t lds, const char* fmt, ...)
+    __attribute__((format(printf, 5, 6)));
+
 }  // namespace wise

@@ -279,6 +279,10 @@ __global__ void __launch_bounds__(kScanThreads) scan_rows_kernel(int32_t* row_pt
 template <int EPL>
 hipError_t launch_select_t(const SelectParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)((p.n_rows + kSelWaves - 1) / kSelWaves);
+  if (trace_enabled())
+    trace_launch("select_count/scan/fill", grid, 64 * kSelWaves, 0,
+                 "kind=%d rows=%d n_blocks=%d entries_per_lane=%d eta=%.17g n_steps=%g cap=%d n_mass=%d", p.kind,
+                 p.n_rows, p.nblk, EPL, p.eta, p.n_steps, p.max_blocks, p.n_mass);
   if (grid > 0) hipLaunchKernelGGL(select_count_kernel<EPL>, dim3(grid), dim3(64 * kSelWaves), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -45,6 +45,9 @@
  * - Results are deterministic: identical inputs give bitwise identical
  *   outputs (no atomics on any value path).
  * - No C++ exception crosses this interface.  The library is thread-safe.
+ * - Setting the environment variable WISE_TRACE (to anything but "" or
+ *   "0") prints one line per kernel launch on stderr: kernel, grid,
+ *   workgroup size, dynamic LDS and the launch parameters.
  *
  * Supported shapes: head_dim in {64, 96, 128}; block_size in {16, 32, 64,
  * 128} (16: the attention calls need seq_len % 32 == 0); seq_len <= 65536;

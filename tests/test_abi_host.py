@@ -11,7 +11,8 @@ import pytest
 
 import block_sparse_attention_wise_amd as wise
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
 HEADER = os.path.join(ROOT, "include", "wise.h")
 
 FAKE = 0x10000        # 16-byte aligned, never dereferenced: every call below fails validation first
@@ -284,3 +285,38 @@ def test_noalloc_call_refuses_sizes_beyond_its_buffer():
     empty = wise.WiseDesc(0, 4, 4096, 128, 64, 0.0)
     assert lib.wise_full_attn_accum_noalloc(ctypes.byref(empty), None, None, None, None, None, None) \
         == wise.WISE_OK
+
+
+def test_host_validation_under_sanitizers(tmp_path):
+    """The C ABI's host-side validation built with the host address and
+    undefined-behaviour sanitizers (device code unchanged) and run without a
+    GPU: every invalid call is refused, every empty call succeeds, and the
+    sanitizers report nothing."""
+    import shutil
+    import subprocess
+    root = os.path.dirname(HERE)
+    pkg = os.path.join(root, "block_sparse_attention_wise_amd")
+    objs = [os.path.join(pkg, "_build", f"{n}.o") for n in
+            ("wise_select", "wise_diag", "wise_attn_d64", "wise_attn_d96", "wise_attn_d128")]
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    if not (shutil.which(hipcc) or os.path.exists(hipcc)) or not all(os.path.exists(o) for o in objs):
+        pytest.skip("needs hipcc and the library's built objects")
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined"]
+    common = ["--offload-arch=gfx950", "-O1", "-g", "-std=c++20", "-Xclang", "-target-feature", "-Xclang",
+              "-packed-fp32-ops"]
+    capi_o = str(tmp_path / "wise_capi_san.o")
+    check_o = str(tmp_path / "abi_check_san.o")
+    exe = str(tmp_path / "abi_check_san")
+    for src, out in ((os.path.join(pkg, "csrc", "wise_capi.hip"), capi_o),
+                     (os.path.join(HERE, "abi_sanitize_check.cpp"), check_o)):
+        r = subprocess.run([hipcc, *common, *san, "-c", src, "-o", out], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-3000:]
+    r = subprocess.run([hipcc, "--offload-arch=gfx950", *san, check_o, capi_o, *objs, "-o", exe],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 0, (r.stdout[-2000:], r.stderr[-3000:])
+    assert "all checks passed" in r.stdout
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr[-3000:]

@@ -206,3 +206,29 @@ def test_trajectory_on_a_side_stream():
     stats = check_trajectory_rows(cfg, m1.numpy(), rows, lambda t, b, h, r: outs[t][b, h][r], samples,
                                   lambda b, h: wl.head_steps(b, h, cfg.steps))
     say(f"  {stats['rows']} rows, max-abs {stats['max_abs']:.2e}")
+
+
+def test_trace_prints_one_line_per_launch():
+    """WISE_TRACE=1 (read once per process, so in a child process): one
+    stderr line per kernel launch naming the kernel, grid and parameters."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import sys, torch; sys.path.insert(0, %r)\n"
+            "import block_sparse_attention_wise_amd as w\n"
+            "q = torch.randn(1, 2, 256, 64, device='cuda').to(torch.bfloat16)\n"
+            "m = torch.zeros(1, 2, 4, 4, device='cuda')\n"
+            "w.wise_full_attn_accum(q, q, q, m, 64)\n"
+            "rp, ci = w.wise_select_support(m, 1, 0.9, 64, 64)\n"
+            "w.wise_sparse_attn(q, q, q, rp, ci, 64)\n"
+            "torch.cuda.synchronize()\n") % root
+    say("WISE_TRACE child process")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120,
+                       env=dict(os.environ, WISE_TRACE="1"))
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stderr.splitlines() if ln.startswith("[wise] ")]
+    assert len(lines) == 3, lines
+    assert "mode=dense+mass" in lines[0] and "grid=" in lines[0] and "lds=" in lines[0]
+    assert lines[1].startswith("[wise] select_count/scan/fill") and "rows=8" in lines[1]
+    assert "mode=sparse" in lines[2] and "head_dim=64 block=64" in lines[2]
