@@ -254,10 +254,9 @@ def discovery_forms(wise, torch, cfg, qs, ks, vs, mass, ws, o, reps=3):
         "on_chip": lambda t: wise.wise_full_attn_accum(qs[t], ks[t], vs[t], mass, B, o=o),
         "workspace": lambda t: wise.wise_full_attn_accum_ws(qs[t], ks[t], vs[t], mass, B, o=o, workspace=ws),
     }
-    out = {}
-    for name, fn in forms.items():
-        xs = []
-        for r in range(reps + 1):
+    xs = {name: [] for name in forms}
+    for r in range(reps + 1):            # the forms alternate, pass by pass; pass 0 warms up
+        for name, fn in forms.items():
             mass.zero_()
             e0.record(stream)
             for t in range(td):
@@ -265,9 +264,9 @@ def discovery_forms(wise, torch, cfg, qs, ks, vs, mass, ws, o, reps=3):
             e1.record(stream)
             e1.synchronize()
             if r > 0:
-                xs.append(e0.elapsed_time(e1) / td)
-        out[name] = float(np.median(xs))
+                xs[name].append(e0.elapsed_time(e1) / td)
     mass.zero_()
+    out = {name: float(np.median(v)) for name, v in xs.items()}
     return out, min(out, key=out.get)
 
 
@@ -434,9 +433,9 @@ def main(argv=None):
                      dtype=torch.uint8, device=dev)
 
     # The discovery step runs in whichever of its two forms is faster on this
-    # workload (on-chip partials, or partials in the workspace).
-    forms, used_form = discovery_forms(wise, torch, cfg, qs, ks, vs, mass, ws, outs[0])
-    log(f"discovery forms (ms per launch): {forms}; trajectory uses {used_form}")
+    # workload (on-chip partials, or partials in the workspace); chosen after
+    # the warm-up trajectories below.
+    used_form = "workspace"
 
     def accum(t, m):
         if used_form == "on_chip":
@@ -471,6 +470,11 @@ def main(argv=None):
         del src, dst
 
     log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        trajectory()
+    torch.cuda.synchronize()
+    forms, used_form = discovery_forms(wise, torch, cfg, qs, ks, vs, mass, ws, outs[0], reps=5)
+    log(f"discovery forms (ms per launch): {forms}; trajectory uses {used_form}")
     for _ in range(args.warmup):
         trajectory()
     torch.cuda.synchronize()
@@ -682,8 +686,11 @@ def main(argv=None):
             cfg_b = cfg.with_(block=Bs)
             nb_b = cfg.seq_len // Bs
             m_b = torch.zeros(cfg.batch, cfg.heads, nb_b, nb_b, dtype=torch.float32, device=dev)
+            ws_b = torch.empty(max(wise.wise_accum_workspace_bytes(cfg.batch, cfg.heads, cfg.seq_len, D, Bs), 16),
+                               dtype=torch.uint8, device=dev)
+            forms_b, _ = discovery_forms(wise, torch, cfg_b, qs, ks, vs, m_b, ws_b, outs[0])
             for t in range(td):
-                wise.wise_full_attn_accum(qs[t], ks[t], vs[t], m_b, Bs, o=outs[t])
+                wise.wise_full_attn_accum_ws(qs[t], ks[t], vs[t], m_b, Bs, o=outs[t], workspace=ws_b)
             rp_b, ci_b = wise.wise_select_support(m_b, td, cfg.eta, D, Bs, cfg.cap)
             fcb = flop_counts(cfg_b, rp_b.cpu().numpy())
 
@@ -695,8 +702,9 @@ def main(argv=None):
                                     "sparse_ms": round(sp, 4),
                                     "sparse_tflops_exec": round(fcb["sparse_exec"] / (sp * 1e-3) / 1e12, 2),
                                     "late_step_speedup_vs_dense": round(k2_ms_ref / sp, 3),
-                                    "ideal_speedup_1_over_density": round(1.0 / fcb["density_adm"], 3)}
-            del m_b, rp_b, ci_b
+                                    "ideal_speedup_1_over_density": round(1.0 / fcb["density_adm"], 3),
+                                    "discovery_ms": {n: round(v, 4) for n, v in forms_b.items()}}
+            del m_b, rp_b, ci_b, ws_b
 
     if variants is not None:
         k2 = med(dts) / n_late

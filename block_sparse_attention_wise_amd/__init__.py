@@ -249,7 +249,7 @@ def wise_full_attn_accum(q, k, v, mass, block_size: int, o=None, softmax_scale: 
 
 
 def wise_accum_workspace_bytes(batch: int, heads: int, seq_len: int, head_dim: int, block_size: int) -> int:
-    """Bytes of workspace wise_full_attn_accum_ws needs (0 for blocks 16 and 32)."""
+    """Bytes of workspace wise_full_attn_accum_ws needs (0 for block 16)."""
     d = WiseDesc(batch, heads, seq_len, head_dim, _block(block_size), 0.0)
     n = load_library().wise_full_attn_accum_workspace_bytes(ctypes.byref(d))
     if n < 0:

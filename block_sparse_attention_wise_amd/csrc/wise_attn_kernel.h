@@ -307,7 +307,7 @@ __global__ void __launch_bounds__(64 * (BLK / 32) * RPW, 2) wise_attn_kernel(Att
   static_assert(LPR == 1 || (LPR == 2 && BLK == 32 && KT == 32 && RPW <= 2 && MODE != kDense),
                 "logical sub-blocks: block 16 on 32 x 32 tiles, at most two rows per workgroup");
   static_assert(RPW * LPR * LPR <= 8, "list-entry tag bits");
-  static_assert(MODE != kDenseMassWs || (LPR == 1 && BLK >= 64), "workspace mass mode: blocks 64 and 128");
+  static_assert(MODE != kDenseMassWs || (LPR == 1 && BLK >= 32), "workspace mass mode: blocks 32, 64 and 128");
   constexpr bool kMass1 = (MODE == kDenseMass || MODE == kDenseMassWs);   // one-pass block mass
 
   using Dm = DmaTile<D, KT, Sh::kThreads>;
@@ -1254,7 +1254,7 @@ hipError_t launch_attn_blk(int mode_in, const AttnParams& p, hipStream_t stream)
     case kSparse: return launch_cfg<D, BLK, kSparse>(c, p, stream);
     case kMassTwoPass: return launch_cfg<D, BLK, kMassTwoPass>(c, p, stream);
     case kDenseMassWs:
-      if constexpr (BLK >= 64) return launch_cfg<D, BLK, kDenseMassWs>(c, p, stream);
+      if constexpr (BLK >= 32) return launch_cfg<D, BLK, kDenseMassWs>(c, p, stream);
       else return hipErrorInvalidValue;
     default: return launch_cfg<D, BLK, kDenseMass>(c, p, stream);
   }
@@ -1304,10 +1304,10 @@ size_t attn_lds_bytes_blk(int mode_in, int nblk) {
   return c.kt ? cfg_lds<D, BLK>(c.kt, c.rpw, mode, nblk) : 0;
 }
 
-// The workspace mass mode exists for blocks 64 and 128; smaller blocks run
-// the LDS mass launches (their partials are small).
+// The workspace mass mode exists for blocks 32, 64 and 128; block 16 runs
+// the LDS mass launches (two logical blocks per tile, small partials).
 inline int mode_for_block(int block, int mode) {
-  return (mode == kDenseMassWs && block < 64) ? kDenseMass : mode;
+  return (mode == kDenseMassWs && block < 32) ? kDenseMass : mode;
 }
 
 template <int D>

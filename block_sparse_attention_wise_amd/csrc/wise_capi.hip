@@ -161,9 +161,9 @@ wise_status_t run_attn(const wise_attn_desc_t* d, int mode, const void* q, const
 }
 
 // Workspace of the mass launch: one fp32 partial per (row, key block, query
-// of the row), for blocks 64 and 128; smaller blocks need none.
+// of the row), for blocks 32, 64 and 128; block 16 needs none.
 int64_t accum_workspace_bytes(const wise_attn_desc_t* d, int32_t nblk, int64_t n_rows) {
-  if (d->block_size < 64) return 0;
+  if (d->block_size < 32) return 0;
   return n_rows * (int64_t)nblk * d->block_size * 4;
 }
 

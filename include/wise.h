@@ -135,11 +135,12 @@ wise_status_t wise_full_attn_accum(const wise_attn_desc_t* desc, const void* q, 
  * The discovery step of wise_full_attn_accum (the same Eq. 2 output and the
  * same Section 5.1, Eq. (5) block mass, added into mass), with the
  * per-(query, key block) partial sums of Eq. (5) kept in a caller-owned
- * workspace in device memory instead of on chip.  For block sizes 64 and
- * 128 this runs the mass launch at the dense kernel's tile size and
- * occupancy at every sequence length, where wise_full_attn_accum has to
- * shrink its tiles or walk the keys twice as rows grow.  For block sizes
- * 16 and 32 the call is wise_full_attn_accum and the workspace is unused.
+ * workspace in device memory instead of on chip.  For block sizes 32, 64
+ * and 128 this runs the mass launch at the dense kernel's tile size and
+ * occupancy in one pass over the keys at every sequence length, where
+ * wise_full_attn_accum has to shrink its tiles or walk the keys twice as
+ * rows grow (and always walks them twice at block 32).  For block size 16
+ * the call is wise_full_attn_accum and the workspace is unused.
  *
  * q, k, v, o, mass: as in wise_full_attn_accum.
  * workspace: device memory of at least
@@ -165,8 +166,8 @@ wise_status_t wise_full_attn_accum_ws(const wise_attn_desc_t* desc, const void* 
  *
  * Limit: wise_full_attn_accum_workspace_bytes(desc) must not exceed the
  * buffer (for example 32 heads x 4096 keys at block 64 need 32 MiB), else
- * WISE_ERR_CAPACITY with nothing launched.  Block sizes 16 and 32 need no
- * buffer and run wise_full_attn_accum.
+ * WISE_ERR_CAPACITY with nothing launched.  Block size 16 needs no buffer
+ * and runs wise_full_attn_accum.
  * Nothing in the buffer must start at zero: every partial is written before
  * it is read.  All calls on one GPU share its buffer, so two calls that
  * overlap in time on that GPU (on different streams, or from different host
@@ -180,8 +181,8 @@ wise_status_t wise_full_attn_accum_noalloc(const wise_attn_desc_t* desc, const v
 int64_t wise_full_attn_accum_noalloc_max_bytes(void);
 
 /* Workspace bytes wise_full_attn_accum_ws needs for this descriptor:
- * batch * heads * n_blocks^2 * block_size * 4 for block sizes 64 and 128,
- * 0 for 16 and 32; -1 for an invalid descriptor. */
+ * batch * heads * n_blocks^2 * block_size * 4 for block sizes 32, 64 and
+ * 128, 0 for 16; -1 for an invalid descriptor. */
 int64_t wise_full_attn_accum_workspace_bytes(const wise_attn_desc_t* desc);
 
 /*

@@ -70,7 +70,7 @@ def test_short_last_block_counts(seq, blk, nb):
     """n_blocks = ceil(seq_len / block_size): sizes that depend on it follow."""
     _lib()
     assert wise.wise_select_max_nnz(1, 2, seq, 64, blk, 0) == 2 * nb * (nb + 1) // 2
-    want = 2 * nb * nb * blk * 4 if blk >= 64 else 0
+    want = 2 * nb * nb * blk * 4 if blk >= 32 else 0
     assert wise.wise_accum_workspace_bytes(1, 2, seq, 64, blk) == want
 
 
@@ -249,7 +249,7 @@ def test_accum_workspace_size_and_arguments():
     lib = _lib()
     for blk, nb in ((64, 8), (128, 4), (32, 8), (16, 16)):
         d = _desc(b=2, h=3, s=blk * nb, d=64, blk=blk)
-        want = 2 * 3 * nb * nb * blk * 4 if blk >= 64 else 0
+        want = 2 * 3 * nb * nb * blk * 4 if blk >= 32 else 0
         assert lib.wise_full_attn_accum_workspace_bytes(ctypes.byref(d)) == want
         assert wise.wise_accum_workspace_bytes(2, 3, blk * nb, 64, blk) == want
     assert lib.wise_full_attn_accum_workspace_bytes(None) == -1
