@@ -14,7 +14,8 @@ record for the sparse kernel and the fp64 CPU oracle timed on a sample
 (discovery, selection and late phases, plus a single-thread sample).
 
 A sweep over the other workloads (8K, 16K and 32K context, the wide-head
-batched workload and the long block-128 workload) follows, each with its own
+batched workload, the long block-128 workload, and the 4K inputs selected at
+eta = 0.6, about 15% of the full block grid) follows, each with its own
 discovery steps, selection and a few reuse steps: late-step TFLOP/s, the
 fraction of the bf16 peak, speedup over the dense kernel next to
 1/density, and the same-backend comparison, every timing as median and
@@ -55,7 +56,7 @@ def parse(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of timed CPU-oracle work")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the per-workload sweep (8K, 16K, 32K, wide, long)")
-    ap.add_argument("--sweep", default="ctx8k,ctx16k,ctx32k,wide,long",
+    ap.add_argument("--sweep", default="ctx8k,ctx16k,ctx32k,wide,long,ctx4k_eta06",
                     help="workloads of the sweep (comma-separated)")
     ap.add_argument("--sweep-passes", type=int, default=7)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",

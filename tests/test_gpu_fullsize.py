@@ -42,7 +42,7 @@ def _samples(cfg, rng):
     return out
 
 
-@pytest.mark.parametrize("name", ["ctx4k", "ctx8k", "ctx16k", "ctx32k", "wide", "long", "gqa4k"])
+@pytest.mark.parametrize("name", ["ctx4k", "ctx8k", "ctx16k", "ctx32k", "wide", "long", "gqa4k", "ctx4k_eta06"])
 def test_full_size_trajectory(name):
     cfg = CONFIGS[name]
     n_steps = cfg.steps if name == "ctx4k" else cfg.td + 2
