@@ -98,7 +98,8 @@ def sparse_bytes(cfg, nnz, n_rows):
     return qkvo + csr
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_ctx4k_hbm_traffic.md")
+def traffic_file(name: str) -> str:
+    return os.path.join(ROOT, "profiles", f"sparse_attn_{name}_hbm_traffic.md")
 KERNEL_SOURCES = ["block_sparse_attention_wise_amd/csrc/wise_attn_kernel.h",
                   "block_sparse_attention_wise_amd/csrc/wise_attn_d128.hip"]
 
@@ -118,13 +119,14 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per sparse launch from the committed rocprofv3 counter runs
-    (FETCH_SIZE / WRITE_SIZE, copy-calibrated), or None when the attention
-    kernel source changed since they were taken."""
+def measured_traffic(name: str = "ctx4k"):
+    """HBM bytes per sparse launch of workload ``name`` from the committed
+    rocprofv3 counter runs (FETCH_SIZE / WRITE_SIZE, copy-calibrated), or
+    None when there is no record or the attention kernel source changed
+    since it was taken."""
     try:
         kv = {}
-        with open(TRAFFIC_FILE) as fh:
+        with open(traffic_file(name)) as fh:
             for line in fh:
                 if ":" in line and line.split(":")[0].strip() in (
                         "kernel_source_hash", "sparse_read_bytes_per_launch",
@@ -361,6 +363,7 @@ def run_sweep(names, passes, wise, torch, dev, n_late=4):
         m = lambda xs: float(np.median(xs))
         t4, t2, t1, t3, tf = m(k4), m(k2), m(k1), m(k3), m(kf)
         ideal = 1.0 / fc["density_adm"]
+        traffic = measured_traffic(name)
         out[name] = {
             "workload": (f"batch {cfg.batch}, {cfg.heads} heads, head_dim {D}, seq {cfg.seq_len}, block {B}, "
                          f"T {T}, td {td}, eta {cfg.eta}, cap {cfg.cap}"),
@@ -368,6 +371,8 @@ def run_sweep(names, passes, wise, torch, dev, n_late=4):
             "density_full_grid": round(fc["density_full"], 4),
             "sparse_tflops_exec": round(fc["sparse_exec"] / (t4 * 1e-3) / 1e12, 2),
             "frac_bf16_peak_algorithmic": round(fc["sparse_alg"] / (t4 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "hbm_traffic_bytes_per_launch": traffic,
+            "hbm_GBps": round(traffic / (t4 * 1e-3) / 1e9, 1) if traffic else None,
             "late_step_speedup_vs_dense": round(t2 / t4, 3),
             "ideal_speedup_1_over_density": round(ideal, 3),
             "speedup_over_ideal": round(t2 / t4 / ideal, 3),
@@ -620,7 +625,7 @@ def main(argv=None):
     value = fc["sparse_exec"] / (k4_ms * 1e-3) / 1e12
     alg_tflops = fc["sparse_alg"] / (k4_ms * 1e-3) / 1e12
     step_ms = wall / args.steps * 1e3
-    traffic = measured_traffic() if args.config == "ctx4k" else None
+    traffic = measured_traffic(args.config)
 
     result = {
         "metric": METRIC,
